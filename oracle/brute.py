@@ -1,0 +1,75 @@
+"""Brute-force paged decode attention in pure Python (tiny inputs only).
+
+TEST INFRASTRUCTURE ONLY (imported by the tests and nothing else).  It shares
+no code with the numpy oracle: every token is found through its own
+logical-to-physical lookup (page index and in-page offset from the page
+table, as PagedAttentionMemory translates addresses in the zskr.cn ATB
+PagedAttention article), every score is a Python loop over head_dim, and the
+softmax uses math.exp over a list.  It exists to pin the oracle's gather,
+head grouping and softmax against an independent spelling of the definition.
+"""
+from __future__ import annotations
+
+import math
+
+PAGE_TOKENS = 16
+
+
+def logical_to_physical(table_row, token: int):
+    """(physical block, slot) of logical token `token` of one sequence."""
+    page_index = token // PAGE_TOKENS
+    offset_in_page = token % PAGE_TOKENS
+    return int(table_row[page_index]), offset_in_page
+
+
+def brute_decode(q, k_pool, v_pool, block_table, context_lens, scale,
+                 k_scale=None, v_scale=None):
+    """Nested lists out[b][h][d] and lse[b][h]."""
+    B = len(q)
+    Hq = len(q[0])
+    D = len(q[0][0])
+    Hkv = len(k_pool[0][0])
+    G = Hq // Hkv
+    out, lse = [], []
+    for b in range(B):
+        L = int(context_lens[b])
+        ob, lb = [], []
+        for h in range(Hq):
+            g = h // G
+            scores, vals = [], []
+            for t in range(L):
+                blk, off = logical_to_physical(block_table[b], t)
+                ks = float(k_scale[blk][off][g]) if k_scale is not None else 1.0
+                vs = float(v_scale[blk][off][g]) if v_scale is not None else 1.0
+                acc = 0.0
+                for d in range(D):
+                    acc += float(q[b][h][d]) * (float(k_pool[blk][off][g][d]) * ks)
+                scores.append(float(scale) * acc)
+                vals.append([float(v_pool[blk][off][g][d]) * vs for d in range(D)])
+            if L == 0:
+                ob.append([0.0] * D)
+                lb.append(-math.inf)
+                continue
+            top = max(scores)
+            w = [math.exp(s - top) for s in scores]
+            tot = math.fsum(w)
+            ob.append([math.fsum(w[t] * vals[t][d] for t in range(L)) / tot for d in range(D)])
+            lb.append(top + math.log(tot))
+        out.append(ob)
+        lse.append(lb)
+    return out, lse
+
+
+def brute_write(k_pool, v_pool, k_new, v_new, slots):
+    """Element-by-element write of new tokens, as nested lists (tiny pools)."""
+    kp = [[[list(r) for r in tok] for tok in blk] for blk in k_pool]
+    vp = [[[list(r) for r in tok] for tok in blk] for blk in v_pool]
+    for i, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        blk, off = slot // PAGE_TOKENS, slot % PAGE_TOKENS
+        for g in range(len(k_new[i])):
+            for d in range(len(k_new[i][g])):
+                kp[blk][off][g][d] = k_new[i][g][d]
+                vp[blk][off][g][d] = v_new[i][g][d]
+    return kp, vp
