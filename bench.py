@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark: paged-attention decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the hot path over one batch: the KV write of each
+sequence's new token into its slot (fp16 copy, or quantising int8 write),
+then paged decode attention over every sequence's context (split-K partition
+kernel, plus the log-sum-exp merge when the context spans several
+partitions).  Inputs are seeded synthetic tensors already resident in HBM.
+
+Headline workload: one Llama2-7B-shaped layer - 32 sequences x 4096 tokens,
+32 query / 32 kv heads, head_dim 128, fp16, 16-token blocks, block tables 85 %
+contiguous.  metric value = ideal KV bytes / step time (GB/s); the other
+workloads are measured the same way and reported under "others".
+
+"roofline" describes the dominant kernel (the decode partition kernel):
+achieved = its algorithmic bytes (the KV bytes it must read) / its mean
+duration, timed with HIP events recorded on the stream it runs on, around
+each launch inside the timed steps.  "traffic" comes from rocprofv3 counter
+summaries committed under profiles/ and is null unless they were taken on
+the current kernel source.  "cpu_baseline" times the fp64 CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "paged-attn decode: achieved KV HBM GB/s (% of peak) and sequences/s per layer"
+HEADLINE = "llama2_7b"
+OTHERS = ["gqa70b_mixed", "prefix_shared", "long128k_int8", "tiny_gqa"]
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_238_amd", "csrc", "decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--others", default=",".join(OTHERS),
+                    help="comma list of extra workloads to report ('' for none)")
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="override the partition size (-1: the workload's own choice)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("decode.hip", "merge.hip", "pa_internal.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_238_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Case:
+    """Device-resident inputs of one workload plus its step."""
+
+    def __init__(self, pa, torch, gen, name, partition_size, dev):
+        self.pa, self.torch, self.name = pa, torch, name
+        wl = gen.make(name, poison=False)
+        self.wl = wl
+        vals = gen.fill_torch(wl, dev)
+        self.v = vals
+        self.bt = torch.from_numpy(wl.block_table).to(dev)
+        self.cl = torch.from_numpy(wl.context_lens).to(dev)
+        self.slots = torch.from_numpy(wl.new_slots).to(dev)
+        P = wl.partition_size if partition_size < 0 else partition_size
+        self.P = pa.partition_size(wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim,
+                                   wl.max_context_len, P)
+        self.n_part = max(1, -(-wl.max_context_len // self.P))
+        need = pa.workspace_size(wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim,
+                                 wl.max_context_len, self.P)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(vals["q"])
+        self.int8 = wl.kv_dtype == "int8"
+        self.kv_bytes = gen.kv_ideal_bytes(wl)                # unique bytes
+        self.kv_bytes_logical = gen.kv_ideal_bytes(wl, unique=False)
+
+    def write(self):
+        v = self.v
+        if self.int8:
+            self.pa.write_kv_int8(v["k_new"], v["v_new"], self.slots, v["k_pool"], v["v_pool"],
+                                  v["k_scale"], v["v_scale"])
+        else:
+            self.pa.write_kv(v["k_new"], v["v_new"], self.slots, v["k_pool"], v["v_pool"])
+
+    def decode_kernel(self):
+        """The partition kernel alone: direct output when one partition
+        covers the context, else the partition records."""
+        v, wl = self.v, self.wl
+        if self.n_part == 1:
+            if self.int8:
+                self.pa.decode_int8(v["q"], v["k_pool"], v["v_pool"], v["k_scale"], v["v_scale"],
+                                    self.bt, self.cl, scale=wl.scale, partition_size=self.P,
+                                    max_context_len=wl.max_context_len, out=self.out,
+                                    workspace=self.ws)
+            else:
+                self.pa.decode(v["q"], v["k_pool"], v["v_pool"], self.bt, self.cl, scale=wl.scale,
+                               partition_size=self.P, max_context_len=wl.max_context_len,
+                               out=self.out, workspace=self.ws)
+        else:
+            self.pa.decode_partials(v["q"], v["k_pool"], v["v_pool"], self.bt, self.cl, self.ws,
+                                    scale=wl.scale, partition_size=self.P,
+                                    max_context_len=wl.max_context_len,
+                                    k_scale=v.get("k_scale"), v_scale=v.get("v_scale"))
+
+    def merge(self):
+        if self.n_part > 1:
+            wl = self.wl
+            self.pa.merge_partials(self.ws, self.cl, wl.q_heads, wl.head_dim, self.P,
+                                   wl.max_context_len, out=self.out)
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.write()
+            self.decode_kernel()
+            self.merge()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in ev:
+            self.write()
+            a.record()
+            self.decode_kernel()
+            b.record()
+            self.merge()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
+        return wall, kern_ms
+
+
+def summarize(case, wall, kern_ms, steps):
+    wl = case.wl
+    step_s = wall / steps
+    kmean = sum(kern_ms) / len(kern_ms) / 1e3
+    med = kern_ms[len(kern_ms) // 2] / 1e3
+    return {
+        "workload": wl.name, "batch": wl.batch, "q_heads": wl.q_heads, "kv_heads": wl.kv_heads,
+        "head_dim": wl.head_dim, "block_size": 16, "kv_dtype": wl.kv_dtype,
+        "max_context_len": wl.max_context_len,
+        "mean_context_len": round(float(wl.context_lens.mean()), 1),
+        "partition_size": case.P, "n_part": case.n_part,
+        "kv_bytes": case.kv_bytes, "kv_bytes_logical": case.kv_bytes_logical,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "step_GBps": round(case.kv_bytes / step_s / 1e9, 1),
+        "seq_per_s": round(wl.batch / step_s, 1),
+        "decode_kernel_us_mean": round(kmean * 1e6, 2),
+        "decode_kernel_us_median": round(med * 1e6, 2),
+        "decode_kernel_GBps": round(case.kv_bytes / kmean / 1e9, 1),
+        "decode_kernel_frac_of_peak": round(case.kv_bytes / kmean / 1e9 / PEAK_HBM_GBS, 4),
+    }
+
+
+def traffic_for(name):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_partition_{name}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("source_hash") != source_hash():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s):
+    """fp64 oracle on the host: whole sequences (all heads) in order until
+    the time budget is spent; single thread (BLAS pinned to one)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ref
+    wl = case.wl
+    v = case.v
+    host = {k: v[k].cpu().numpy() for k in ("q", "k_pool", "v_pool")}
+    ks = v["k_scale"].cpu().numpy() if case.int8 else None
+    vs = v["v_scale"].cpu().numpy() if case.int8 else None
+    done_bytes, done_seqs = 0, 0
+    per_tok = case.kv_bytes_logical / max(1, int(wl.context_lens.sum()))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for b in range(wl.batch):
+            rows = [(b, h) for h in range(wl.q_heads)]
+            ref.ref_decode(host["q"], host["k_pool"], host["v_pool"], wl.block_table,
+                           wl.context_lens, wl.scale, ks, vs, rows=rows)
+            done_seqs += 1
+            done_bytes += int(wl.context_lens[b]) * per_tok
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seq_per_s": round(done_seqs / dt, 3),
+            "sample": f"{done_seqs} of {wl.batch} sequences of {wl.name} (all "
+                      f"{wl.q_heads} heads each), fp64 numpy, one thread, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path runs on a single device)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_238_amd as pa
+    from workloads import gen
+
+    dev = torch.device("cuda:0")
+    head = Case(pa, torch, gen, args.workload, args.partition_size, dev)
+    wall, kern = head.run(args.steps, args.warmup)
+    s = summarize(head, wall, kern, args.steps)
+    print(f"[bench] {args.workload}: {s['ms_per_step']} ms/step, decode kernel "
+          f"{s['decode_kernel_us_mean']} us = {s['decode_kernel_GBps']} GB/s", file=sys.stderr,
+          flush=True)
+    others = []
+    for name in [n for n in args.others.split(",") if n and n != args.workload]:
+        c = Case(pa, torch, gen, name, -1, dev)
+        w2, k2 = c.run(max(20, args.steps // 2), max(5, args.warmup // 2))
+        o = summarize(c, w2, k2, max(20, args.steps // 2))
+        others.append(o)
+        print(f"[bench] {name}: {o['ms_per_step']} ms/step, decode kernel "
+              f"{o['decode_kernel_us_mean']} us = {o['decode_kernel_GBps']} GB/s",
+              file=sys.stderr, flush=True)
+        del c
+        torch.cuda.empty_cache()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(head, args.cpu_seconds)
+    achieved = s["decode_kernel_GBps"]
+    line = {
+        "metric": METRIC,
+        "value": s["step_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": s["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "accumulate": "f32",
+        "data": "synthetic (seeded N(0,1) fp16 K/V/Q; block tables per workload recipe)",
+        "pct_of_peak": round(100 * s["step_GBps"] / PEAK_HBM_GBS, 2),
+        "seq_per_s": s["seq_per_s"],
+        "config": {k: s[k] for k in ("workload", "batch", "q_heads", "kv_heads", "head_dim",
+                                     "block_size", "kv_dtype", "max_context_len",
+                                     "partition_size", "n_part", "kv_bytes")},
+        "roofline": {"bound": "hbm", "kernel": "decode_valu_kernel (partition)",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes_per_launch": s["kv_bytes"],
+                     "launch_us_mean": s["decode_kernel_us_mean"],
+                     "traffic": traffic_for(args.workload),
+                     "source_hash": source_hash()},
+        "cpu_baseline": cpu,
+        "others": others,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+/*
+ * pa.h - paged-attention decode over a block-paged KV cache, for AMD MI355X
+ * (gfx950).  C ABI of libpa.so.
+ *
+ * Sources (the three web pages on KV-cache paging):
+ *   [ATB-KV]  adg.csdn.net article on ATB's KV Cache management: section
+ *             "Paged KV Cache" (fixed 16-token blocks allocated on demand),
+ *             "Prefix Caching" (one prompt prefix's blocks shared by many
+ *             requests), "显存碎片问题" (scattered blocks).
+ *   [KV-OPT]  discosf.com article "KV Cache 优化与显存管理": section
+ *             "二、优化方向" (logically contiguous tokens on physically
+ *             non-contiguous pages; grouped query heads sharing one K/V
+ *             head; FP16 -> INT8 cache), section "三、实现示例"
+ *             (PhysicalPagePool.write_page, KVCacheQuantizer per_channel
+ *             quantize / dequantize).
+ *   [ATB-PA]  zskr.cn article on ATB's PagedAttention: section
+ *             "PagedAttention 的 Attention 计算修改" (PagedAttentionKernel:
+ *             Q [batch, num_heads, d_head], K/V pages, page_table
+ *             [request, max_pages], output [batch, num_heads, d_head];
+ *             per-page online softmax), "踩坑一" (page table staged on chip
+ *             once), "踩坑三" (WriteKV appends a token's K, V into its page).
+ *
+ * Layout (all tensors C-contiguous, every pointer a device pointer owned by
+ * the caller unless stated otherwise):
+ *   q, out        fp16  [batch, q_heads, head_dim]
+ *   k_pool,v_pool fp16 or int8 [num_blocks, block_size, kv_heads, head_dim]
+ *   k_scale,      fp32  [num_blocks, block_size, kv_heads]   (int8 pools:
+ *   v_scale             one scale per token and kv head)
+ *   block_table   int32 [batch, max_blocks]; entry j of row b is the physical
+ *                       block holding logical tokens 16j .. 16j+15 of b
+ *   context_lens  int32 [batch]; tokens of sequence b, including the newest
+ *   slot_mapping  int32 [num_tokens]; slot = block * block_size + offset
+ *   lse_out       fp32  [batch, q_heads] natural-log log-sum-exp of the
+ *                       scaled scores (optional, may be NULL)
+ * Query head h reads kv head h / (q_heads / kv_heads).
+ *
+ * Behaviour common to every entry point:
+ *   - block_size must be 16, head_dim 64 or 128, q_heads / kv_heads in
+ *     {1, 2, 4, 8, 16}.
+ *   - Argument errors return a nonzero pa_status before anything is
+ *     launched.  Launch failures return PA_ERR_HIP.  Device-side faults
+ *     surface at the caller's next synchronisation, as in HIP.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = null stream) and
+ *     is asynchronous.  The library allocates no memory, keeps no state
+ *     between calls and retains no pointer after it returns.  Nothing
+ *     throws or aborts across this ABI.
+ *   - Caller contracts that are not checked on the host (they would need a
+ *     device synchronisation): 0 <= block_table[b][j] < num_blocks for
+ *     j < ceil(L_b / 16); 0 <= L_b <= max_context_len.  The kernels check
+ *     both on the device without faulting: a sequence that breaks either
+ *     gets NaN in every element of its output rows.  Entries past
+ *     ceil(L_b / 16) are never read.  Tokens t >= L_b of the last block
+ *     never influence the output, whatever those slots hold.
+ *   - Results are deterministic: no floating-point atomics, fixed
+ *     reduction order for a given (shape, partition_size).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* non-positive size, q_heads % kv_heads != 0,
+                             max_context_len > max_blocks * block_size, ... */
+  PA_ERR_UNSUPPORTED = 3, /* block_size != 16, head_dim not 64/128, group not
+                             in {1,2,4,8,16}, partition_size not a positive
+                             multiple of 16 (or 0) */
+  PA_ERR_WORKSPACE = 4,   /* workspace smaller than pa_decode_workspace_size
+                             (the library never allocates) */
+  PA_ERR_HIP = 5          /* a kernel launch failed */
+} pa_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pa_status_string(int status);
+
+/*
+ * KV write ("reshape and cache"): for every i < num_tokens with
+ * slot_mapping[i] >= 0, copy the rows k_new[i] / v_new[i] ([kv_heads,
+ * head_dim] fp16) into k_pool / v_pool at block slot_mapping[i] / 16,
+ * offset slot_mapping[i] % 16.  [KV-OPT] "三、实现示例" write_page;
+ * [ATB-PA] "踩坑三" WriteKV.
+ *   k_new, v_new  fp16 [num_tokens, kv_heads, head_dim]
+ *   k_pool, v_pool fp16 [num_blocks, block_size, kv_heads, head_dim]
+ * A byte copy: the written rows equal the inputs bit for bit and no other
+ * byte of either pool changes.  Negative slots are skipped; slots >=
+ * num_blocks * 16 are skipped too (never written).  Slots must be unique
+ * and lie in blocks no other sequence shares (copy-on-write is the
+ * caller's job, [ATB-PA] "踩坑三"); duplicates race.  num_tokens == 0 is a
+ * no-op.  Ordered before a following pa_decode on the same stream.
+ */
+int pa_write_kv(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                void* k_pool, void* v_pool, int num_tokens, int num_blocks,
+                int block_size, int kv_heads, int head_dim, void* stream);
+
+/*
+ * KV write into an int8 pool: each new row [head_dim] of k_new / v_new is
+ * quantised with its own scale, absmax(|x|) / 127 in fp32 (a zero scale
+ * becomes 1.0), codes = clip(round-half-even(x / scale), -128, 127), and
+ * codes and scale are stored at the slot.  [KV-OPT] "三、实现示例"
+ * KVCacheQuantizer.quantize, per_channel branch (last axis = head_dim);
+ * "二、优化方向" FP16 -> INT8 cache.  Same slot rules as pa_write_kv.
+ *   k_pool, v_pool int8 [num_blocks, block_size, kv_heads, head_dim]
+ *   k_scale, v_scale fp32 [num_blocks, block_size, kv_heads]
+ */
+int pa_write_kv_int8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                     int8_t* k_pool, int8_t* v_pool, float* k_scale, float* v_scale,
+                     int num_tokens, int num_blocks, int block_size, int kv_heads,
+                     int head_dim, void* stream);
+
+/*
+ * Partition size the library uses for these shapes when partition_size is
+ * 0, else partition_size itself (a multiple of 16).  Returns 0 on invalid
+ * arguments.
+ */
+int pa_decode_partition_size(int batch, int q_heads, int kv_heads, int head_dim,
+                             int max_context_len, int partition_size);
+
+/*
+ * Bytes of device workspace pa_decode / pa_decode_int8 need for these
+ * shapes (0 when the whole context fits one partition).  The same shapes
+ * give the partial records pa_decode_partials writes.  Returns 0 on
+ * invalid arguments as well.
+ */
+size_t pa_decode_workspace_size(int batch, int q_heads, int kv_heads, int head_dim,
+                                int max_context_len, int partition_size);
+
+/*
+ * Decode attention, one query token per sequence:
+ *   out[b,h,:] = sum_{t<L_b} softmax_t(scale * q[b,h,:] . K_b[t]) V_b[t]
+ * with K_b[t] = k_pool[block_table[b][t/16], t%16, h/G, :] (V likewise).
+ * [ATB-PA] "PagedAttention 的 Attention 计算修改" (per-page gather and
+ * online softmax; here with the scale, the head index and an fp32
+ * accumulator); [KV-OPT] "二、优化方向" (GQA grouping).
+ *   max_context_len  host-side upper bound on context_lens (sizes the grid;
+ *                    no device-to-host read); <= max_blocks * 16
+ *   scale            usually 1/sqrt(head_dim)
+ *   partition_size   tokens per split-K partition, multiple of 16; 0 =
+ *                    library's choice (pa_decode_partition_size).  Each
+ *                    partition yields (max, sum, unnormalised output) and
+ *                    partitions are merged by log-sum-exp.
+ *   workspace        device buffer of >= pa_decode_workspace_size bytes
+ *                    (may be NULL when that is 0); not shared by
+ *                    concurrent calls
+ * L_b = 0 gives a zero output row and lse = -inf.  fp32 accumulation,
+ * output rounded to fp16 to nearest even.
+ */
+int pa_decode(void* out, float* lse_out, const void* q, const void* k_pool,
+              const void* v_pool, const int32_t* block_table, int max_blocks,
+              const int32_t* context_lens, int max_context_len, int batch, int q_heads,
+              int kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+              int partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode over an int8 cache with fp32 per-(token, kv head) scales: the
+ * cached value is code * scale ([KV-OPT] "三、实现示例" dequantize), folded
+ * into the score (scale_k) and the softmax weight (scale_v) in fp32.
+ */
+int pa_decode_int8(void* out, float* lse_out, const void* q, const int8_t* k_pool,
+                   const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                   const int32_t* block_table, int max_blocks, const int32_t* context_lens,
+                   int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
+                   int block_size, int num_blocks, float scale, int partition_size,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages pa_decode runs, exported for callers that combine
+ * partial results from several sources (for example one sequence's
+ * context split across devices, or a shared prefix attended once and
+ * merged with each private suffix).
+ *
+ * pa_decode_partials / pa_decode_partials_int8: same arguments as
+ * pa_decode / pa_decode_int8 without out and lse_out; always write the
+ * partition records into the workspace, which must hold
+ * pa_decode_workspace_size(..., partition_size resolved, ...) bytes
+ * computed with max_context_len > partition_size, i.e.
+ * n_part = ceil(max_context_len / P) records per (b, h).  Record layout
+ * (P = resolved partition size):
+ *   float2 ml[batch][q_heads][n_part]   (m, l): m = max of the partition's
+ *                                       scores in log2 units
+ *                                       (scale * log2(e) * q.k), l = sum of
+ *                                       2^(s - m)
+ *   float  o[batch][q_heads][n_part][head_dim]  unnormalised sum 2^(s-m) v
+ * Records of partitions at or past ceil(L_b / P) are not written.
+ *
+ * pa_merge_partials: out[b,h] = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
+ * over p < ceil(L_b / P), M = max m_p; lse = ln 2 * (M + log2(den)).
+ */
+int pa_decode_partials(const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, int max_blocks,
+                       const int32_t* context_lens, int max_context_len, int batch,
+                       int q_heads, int kv_heads, int head_dim, int block_size,
+                       int num_blocks, float scale, int partition_size, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+int pa_decode_partials_int8(const void* q, const int8_t* k_pool, const int8_t* v_pool,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_table, int max_blocks,
+                            const int32_t* context_lens, int max_context_len, int batch,
+                            int q_heads, int kv_heads, int head_dim, int block_size,
+                            int num_blocks, float scale, int partition_size,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,
+                      int max_context_len, int batch, int q_heads, int head_dim,
+                      int partition_size, const void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,298 @@
+"""Python binding of libpa.so: paged-attention decode for AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/pa.h.  torch supplies device
+memory and the current stream; nothing here computes attention, and there is
+no CPU fallback: if libpa.so is missing or fails to load, importing this
+package raises.
+
+Functions mirror the C entry points:
+  write_kv(k_new, v_new, slot_mapping, k_pool, v_pool)
+  write_kv_int8(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale)
+  decode(q, k_pool, v_pool, block_table, context_lens, ...)
+  decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, ...)
+  decode_partials(...), decode_partials_int8(...), merge_partials(...)
+  workspace_size(...), partition_size(...)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "PaError", "LIB_PATH", "lib", "status_string", "write_kv", "write_kv_int8",
+    "partition_size", "workspace_size", "decode", "decode_int8", "decode_partials",
+    "decode_partials_int8", "merge_partials", "EXPORTS",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PA_LIB", os.path.join(HERE, "libpa.so"))
+
+# torch ships its own HIP runtime (libamdhip64.so.7).  Import it before
+# loading libpa.so so that libpa.so binds to that runtime by soname; loading
+# libpa.so first would put /opt/rocm's copy in the process under the same
+# soname and torch's device calls would then run on a runtime it was not
+# built against.
+import torch  # noqa: E402,F401
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libpa.so not found at {LIB_PATH}; build it with "
+        "`python -m paged_kv_cache_238_amd.build` (hipcc, gfx950)")
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_z = ctypes.c_size_t
+
+# name -> (restype, argtypes); the full exported surface of include/pa.h
+EXPORTS = {
+    "pa_status_string": (ctypes.c_char_p, [_i]),
+    "pa_write_kv": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
+    "pa_write_kv_int8": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
+    "pa_decode_partition_size": (_i, [_i, _i, _i, _i, _i, _i]),
+    "pa_decode_workspace_size": (_z, [_i, _i, _i, _i, _i, _i]),
+    "pa_decode": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                       _p, _z, _p]),
+    "pa_decode_int8": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
+                            _i, _f, _i, _p, _z, _p]),
+    "pa_decode_partials": (_i, [_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                                _p, _z, _p]),
+    "pa_decode_partials_int8": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
+                                     _i, _f, _i, _p, _z, _p]),
+    "pa_merge_partials": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _z, _p]),
+}
+for _name, (_res, _args) in EXPORTS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+BLOCK_SIZE = 16
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def status_string(status: int) -> str:
+    return lib.pa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise PaError(status, where)
+
+
+# --- torch marshalling -------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, name, dtype, ndim=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def write_kv(k_new, v_new, slot_mapping, k_pool, v_pool) -> None:
+    """Copy token i's K/V rows [kv_heads, head_dim] into slot slot_mapping[i]
+    of the fp16 pools (negative slots skipped)."""
+    torch = _torch()
+    _need(k_pool, "k_pool", torch.float16, 4)
+    dev = k_pool.device
+    _need(v_pool, "v_pool", torch.float16, 4, dev)
+    _need(k_new, "k_new", torch.float16, 3, dev)
+    _need(v_new, "v_new", torch.float16, 3, dev)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1, dev)
+    NB, bs, Hkv, D = k_pool.shape
+    T = k_new.shape[0]
+    if v_pool.shape != k_pool.shape or k_new.shape != (T, Hkv, D) or v_new.shape != k_new.shape \
+            or slot_mapping.shape[0] != T:
+        raise ValueError("write_kv: inconsistent shapes")
+    _check(lib.pa_write_kv(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_pool),
+                           _ptr(v_pool), T, NB, bs, Hkv, D, _stream(k_pool)), "pa_write_kv")
+
+
+def write_kv_int8(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale) -> None:
+    """Quantise token i's K/V rows per (token, kv head) into the int8 pools
+    and their fp32 scales at slot slot_mapping[i]."""
+    torch = _torch()
+    _need(k_pool, "k_pool", torch.int8, 4)
+    dev = k_pool.device
+    _need(v_pool, "v_pool", torch.int8, 4, dev)
+    _need(k_scale, "k_scale", torch.float32, 3, dev)
+    _need(v_scale, "v_scale", torch.float32, 3, dev)
+    _need(k_new, "k_new", torch.float16, 3, dev)
+    _need(v_new, "v_new", torch.float16, 3, dev)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1, dev)
+    NB, bs, Hkv, D = k_pool.shape
+    T = k_new.shape[0]
+    if v_pool.shape != k_pool.shape or k_scale.shape != (NB, bs, Hkv) \
+            or v_scale.shape != k_scale.shape or k_new.shape != (T, Hkv, D) \
+            or v_new.shape != k_new.shape or slot_mapping.shape[0] != T:
+        raise ValueError("write_kv_int8: inconsistent shapes")
+    _check(lib.pa_write_kv_int8(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_pool),
+                                _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), T, NB, bs, Hkv, D,
+                                _stream(k_pool)), "pa_write_kv_int8")
+
+
+def partition_size(batch, q_heads, kv_heads, head_dim, max_context_len, partition_size=0) -> int:
+    return int(lib.pa_decode_partition_size(batch, q_heads, kv_heads, head_dim,
+                                            max_context_len, partition_size))
+
+
+_resolve_partition = partition_size
+
+
+def workspace_size(batch, q_heads, kv_heads, head_dim, max_context_len, partition_size=0) -> int:
+    return int(lib.pa_decode_workspace_size(batch, q_heads, kv_heads, head_dim,
+                                            max_context_len, partition_size))
+
+
+def _decode_args(q, k_pool, v_pool, block_table, context_lens, kv_dtype, max_context_len,
+                 k_scale=None, v_scale=None):
+    torch = _torch()
+    _need(q, "q", torch.float16, 3)
+    dev = q.device
+    _need(k_pool, "k_pool", kv_dtype, 4, dev)
+    _need(v_pool, "v_pool", kv_dtype, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    NB, bs, Hkv, D2 = k_pool.shape
+    if v_pool.shape != k_pool.shape or D2 != D or block_table.shape[0] != B \
+            or context_lens.shape[0] != B:
+        raise ValueError("decode: inconsistent shapes")
+    if k_scale is not None:
+        _need(k_scale, "k_scale", torch.float32, 3, dev)
+        _need(v_scale, "v_scale", torch.float32, 3, dev)
+        if k_scale.shape != (NB, bs, Hkv) or v_scale.shape != k_scale.shape:
+            raise ValueError("decode_int8: scale shapes must be [num_blocks, block_size, kv_heads]")
+    if max_context_len is None:
+        # host bound from the device lengths (one synchronising read); pass it
+        # explicitly to avoid the read
+        max_context_len = int(context_lens.max().item()) if B else 0
+    return B, Hq, Hkv, D, NB, bs, block_table.shape[1], int(max_context_len)
+
+
+def _alloc_out(q, out, return_lse):
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.float16, 3, q.device)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if return_lse else None
+    return out, lse
+
+
+def _workspace(q, B, Hq, Hkv, D, L, P, workspace):
+    torch = _torch()
+    need = workspace_size(B, Hq, Hkv, D, L, P)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small")
+    return workspace
+
+
+def decode(q, k_pool, v_pool, block_table, context_lens, scale=None, partition_size=0,
+           max_context_len=None, out=None, return_lse=False, workspace=None):
+    """fp16 paged decode.  Returns out [B, Hq, D] fp16 (and lse [B, Hq] fp32
+    when return_lse)."""
+    torch = _torch()
+    B, Hq, Hkv, D, NB, bs, MB, L = _decode_args(q, k_pool, v_pool, block_table, context_lens,
+                                                torch.float16, max_context_len)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out, lse = _alloc_out(q, out, return_lse)
+    ws = _workspace(q, B, Hq, Hkv, D, L, partition_size, workspace)
+    _check(lib.pa_decode(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                         _ptr(block_table), MB, _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB,
+                         scale, partition_size, _ptr(ws), ws.numel(), _stream(q)), "pa_decode")
+    return (out, lse) if return_lse else out
+
+
+def decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, scale=None,
+                partition_size=0, max_context_len=None, out=None, return_lse=False,
+                workspace=None):
+    """Paged decode over an int8 cache with fp32 per-(token, kv head) scales."""
+    torch = _torch()
+    B, Hq, Hkv, D, NB, bs, MB, L = _decode_args(q, k_pool, v_pool, block_table, context_lens,
+                                                torch.int8, max_context_len, k_scale, v_scale)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out, lse = _alloc_out(q, out, return_lse)
+    ws = _workspace(q, B, Hq, Hkv, D, L, partition_size, workspace)
+    _check(lib.pa_decode_int8(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                              _ptr(k_scale), _ptr(v_scale), _ptr(block_table), MB,
+                              _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB, scale,
+                              partition_size, _ptr(ws), ws.numel(), _stream(q)),
+           "pa_decode_int8")
+    return (out, lse) if return_lse else out
+
+
+def decode_partials(q, k_pool, v_pool, block_table, context_lens, workspace, scale=None,
+                    partition_size=0, max_context_len=None, k_scale=None, v_scale=None):
+    """Stage 1 of decode: write the per-partition records into `workspace`
+    (uint8 device tensor of >= workspace_size(...) bytes).  Returns the
+    resolved partition size."""
+    torch = _torch()
+    int8 = k_pool.dtype == torch.int8
+    B, Hq, Hkv, D, NB, bs, MB, L = _decode_args(
+        q, k_pool, v_pool, block_table, context_lens, torch.int8 if int8 else torch.float16,
+        max_context_len, k_scale if int8 else None, v_scale if int8 else None)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    if int8:
+        st = lib.pa_decode_partials_int8(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                         _ptr(v_scale), _ptr(block_table), MB, _ptr(context_lens),
+                                         L, B, Hq, Hkv, D, bs, NB, scale, partition_size,
+                                         _ptr(workspace), nbytes, _stream(q))
+    else:
+        st = lib.pa_decode_partials(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), MB,
+                                    _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB, scale,
+                                    partition_size, _ptr(workspace), nbytes, _stream(q))
+    _check(st, "pa_decode_partials")
+    return _resolve_partition(B, Hq, Hkv, D, L, partition_size)
+
+
+def merge_partials(workspace, context_lens, q_heads, head_dim, partition_size, max_context_len,
+                   out=None, return_lse=False):
+    """Stage 2 of decode: log-sum-exp merge of the records in `workspace`."""
+    torch = _torch()
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B = context_lens.shape[0]
+    dev = context_lens.device
+    if out is None:
+        out = torch.empty((B, q_heads, head_dim), dtype=torch.float16, device=dev)
+    lse = torch.empty((B, q_heads), dtype=torch.float32, device=dev) if return_lse else None
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.pa_merge_partials(_ptr(out), _ptr(lse), _ptr(context_lens), int(max_context_len),
+                                 B, q_heads, head_dim, int(partition_size), _ptr(workspace),
+                                 nbytes, _stream(context_lens)), "pa_merge_partials")
+    return (out, lse) if return_lse else out

@@ -1,0 +1,118 @@
+// Log-sum-exp merge of split-K partition records into the final fp16 row.
+//
+// Partition p of sequence b, query head h carries (m_p, l_p, o_p): the max
+// score of its tokens (log2 units), sum of 2^(s - m_p) and the unnormalised
+// sum of 2^(s - m_p) v.  With M = max_p m_p and w_p = 2^(m_p - M):
+//   out = sum_p w_p o_p / sum_p w_p l_p,   lse = ln2 * (M + log2 sum_p w_p l_p).
+// This is the running-max rescaling of the zskr.cn article's PagedAttention
+// kernel (section "PagedAttention 的 Attention 计算修改") applied once
+// across partitions instead of token by token, followed by that kernel's
+// final normalisation and fp16 store.
+//
+// One workgroup of 256 lanes per (sequence, query head): lanes are split
+// into D/4 float4 columns x (1024/D) partition phases; each lane sums its
+// phase's partitions, then the phases are added through LDS in a fixed
+// order (deterministic).
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.693147180559945309f;
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  _Float16 h = (_Float16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
+  constexpr int COLS = D / 4;              // float4 columns
+  constexpr int PH = kThreads / COLS;      // partition phases
+  __shared__ float4 s_acc[PH][COLS];
+  __shared__ float s_den[PH];
+  __shared__ float s_max[kThreads / 64];
+
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, col = tid % COLS, ph = tid / COLS;
+  const size_t row = (size_t)b * p.q_heads + h;
+  const int L = p.context_lens[b];
+
+  if (L < 0 || L > p.max_context_len) {
+    for (int d = tid; d < D; d += kThreads) p.out[row * D + d] = 0x7E00;
+    if (tid == 0 && p.lse) p.lse[row] = __builtin_nanf("");
+    return;
+  }
+  const int n = (L + p.partition_size - 1) / p.partition_size;
+  if (n == 0) {
+    for (int d = tid; d < D; d += kThreads) p.out[row * D + d] = 0;
+    if (tid == 0 && p.lse) p.lse[row] = kNegInf;
+    return;
+  }
+  const float2* ml = p.part_ml + row * p.n_part;
+  const float4* o = reinterpret_cast<const float4*>(p.part_o + row * p.n_part * D);
+
+  // M = max_p m_p
+  float M = kNegInf;
+  for (int i = tid; i < n; i += kThreads) M = fmaxf(M, ml[i].x);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((tid & 63) == 0) s_max[tid >> 6] = M;
+  __syncthreads();
+  M = s_max[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) M = fmaxf(M, s_max[i]);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  for (int i = ph; i < n; i += PH) {
+    const float2 r = ml[i];
+    const float wgt = __builtin_amdgcn_exp2f(r.x - Mu);
+    den = fmaf(wgt, r.y, den);
+    const float4 v = o[(size_t)i * COLS + col];
+    acc.x = fmaf(wgt, v.x, acc.x);
+    acc.y = fmaf(wgt, v.y, acc.y);
+    acc.z = fmaf(wgt, v.z, acc.z);
+    acc.w = fmaf(wgt, v.w, acc.w);
+  }
+  s_acc[ph][col] = acc;
+  if (col == 0) s_den[ph] = den;
+  __syncthreads();
+  if (ph == 0) {
+    float dsum = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < PH; ++k) {
+      dsum += s_den[k];
+      const float4 v = s_acc[k][col];
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    uint16_t* dst = p.out + row * D + col * 4;
+    dst[0] = f32_to_f16_bits(a.x / dsum);
+    dst[1] = f32_to_f16_bits(a.y / dsum);
+    dst[2] = f32_to_f16_bits(a.z / dsum);
+    dst[3] = f32_to_f16_bits(a.w / dsum);
+    if (col == 0 && p.lse) p.lse[row] = (M + log2f(dsum)) * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
+  dim3 grid(p.q_heads, p.batch);
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+  else if (p.head_dim == 64)
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pa

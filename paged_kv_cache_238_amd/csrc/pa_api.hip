@@ -1,0 +1,297 @@
+// C ABI of libpa.so: argument validation, partition sizing, workspace
+// layout and kernel dispatch.  Every check happens on the host before any
+// launch; the library allocates nothing and keeps no state.
+#include "pa.h"
+#include "pa_internal.h"
+
+#include <limits.h>
+
+namespace {
+
+using pa::kBlockTokens;
+
+constexpr int kDefaultPartition = 512;      // tokens per split-K partition
+constexpr int kMaxPartition = 1 << 18;      // block ids of one partition fit LDS
+constexpr float kLog2e = 1.4426950408889634f;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// Shape checks shared by every decode entry point.  0 = ok.
+int check_decode_shapes(int max_blocks, int max_context_len, int batch, int q_heads,
+                        int kv_heads, int head_dim, int block_size, int num_blocks,
+                        int partition_size) {
+  if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
+      max_blocks <= 0 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (batch > 65535 || kv_heads > 65535) return PA_ERR_SHAPE;   // grid y / z limits
+  if (q_heads % kv_heads != 0) return PA_ERR_SHAPE;
+  if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if ((long long)max_context_len > (long long)max_blocks * block_size) return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!supported_group(q_heads / kv_heads)) return PA_ERR_UNSUPPORTED;
+  if (partition_size < 0 || partition_size % kBlockTokens != 0 || partition_size > kMaxPartition)
+    return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int resolve_partition(int batch, int q_heads, int kv_heads, int head_dim, int max_context_len,
+                      int partition_size) {
+  (void)batch; (void)q_heads; (void)kv_heads; (void)head_dim; (void)max_context_len;
+  if (partition_size > 0) return partition_size;
+  return kDefaultPartition;
+}
+
+int num_partitions(int max_context_len, int P) {
+  const int n = (max_context_len + P - 1) / P;
+  return n > 0 ? n : 1;
+}
+
+struct Records {
+  size_t ml_bytes, o_offset, total;
+};
+
+Records record_layout(int batch, int q_heads, int head_dim, int n_part) {
+  Records r;
+  const size_t n = (size_t)batch * q_heads * n_part;
+  r.ml_bytes = n * sizeof(float2);
+  r.o_offset = align_up(r.ml_bytes, 256);
+  r.total = r.o_offset + n * head_dim * sizeof(float);
+  return r;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Shared body of the decode entry points.  mode: 0 = full decode (direct
+// when one partition, else partials + merge), 1 = partials only.
+int decode_common(int mode, void* out, float* lse_out, const void* q, const void* k_pool,
+                  const void* v_pool, const float* k_scale, const float* v_scale, bool int8,
+                  const int32_t* block_table, int max_blocks, const int32_t* context_lens,
+                  int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
+                  int block_size, int num_blocks, float scale, int partition_size,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_pool || !v_pool || !block_table || !context_lens) return PA_ERR_NULL;
+  if (mode == 0 && !out) return PA_ERR_NULL;
+  if (int8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  int st = check_decode_shapes(max_blocks, max_context_len, batch, q_heads, kv_heads, head_dim,
+                               block_size, num_blocks, partition_size);
+  if (st != PA_OK) return st;
+  const int P = resolve_partition(batch, q_heads, kv_heads, head_dim, max_context_len,
+                                  partition_size);
+  const int n_part = num_partitions(max_context_len, P);
+  const bool direct = (mode == 0 && n_part == 1);
+  const Records rec = record_layout(batch, q_heads, head_dim, n_part);
+  if (!direct) {
+    if (!workspace) return PA_ERR_NULL;
+    if (workspace_bytes < rec.total) return PA_ERR_WORKSPACE;
+  }
+  if (batch == 0) return PA_OK;
+
+  pa::DecodeParams p = {};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse_out;
+  p.part_ml = direct ? nullptr : static_cast<float2*>(workspace);
+  p.part_o = direct ? nullptr
+                    : reinterpret_cast<float*>(static_cast<char*>(workspace) + rec.o_offset);
+  p.max_blocks = max_blocks;
+  p.max_context_len = max_context_len;
+  p.batch = batch;
+  p.q_heads = q_heads;
+  p.kv_heads = kv_heads;
+  p.head_dim = head_dim;
+  p.num_blocks = num_blocks;
+  p.partition_size = P;
+  p.n_part = n_part;
+  p.scale_log2 = scale * kLog2e;
+  p.direct = direct ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = status_of(pa::launch_decode(p, int8, s));
+  if (st != PA_OK || direct || mode == 1) return st;
+
+  pa::MergeParams mp = {};
+  mp.part_ml = p.part_ml;
+  mp.part_o = p.part_o;
+  mp.context_lens = context_lens;
+  mp.out = p.out;
+  mp.lse = lse_out;
+  mp.batch = batch;
+  mp.q_heads = q_heads;
+  mp.head_dim = head_dim;
+  mp.partition_size = P;
+  mp.n_part = n_part;
+  mp.max_context_len = max_context_len;
+  return status_of(pa::launch_merge(mp, s));
+}
+
+int check_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                const void* k_pool, const void* v_pool, int num_tokens, int num_blocks,
+                int block_size, int kv_heads, int head_dim) {
+  if (num_tokens < 0 || num_blocks <= 0 || kv_heads <= 0 || head_dim <= 0) return PA_ERR_SHAPE;
+  if (num_tokens > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_NULL;
+  if (!k_pool || !v_pool) return PA_ERR_NULL;
+  if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK: success";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: inconsistent or non-positive shape";
+    case PA_ERR_UNSUPPORTED:
+      return "PA_ERR_UNSUPPORTED: block_size must be 16, head_dim 64/128, group 1/2/4/8/16, "
+             "partition_size a multiple of 16";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch failed";
+    default: return "unknown pa_status";
+  }
+}
+
+int pa_write_kv(const void* k_new, const void* v_new, const int32_t* slot_mapping, void* k_pool,
+                void* v_pool, int num_tokens, int num_blocks, int block_size, int kv_heads,
+                int head_dim, void* stream) {
+  int st = check_write(k_new, v_new, slot_mapping, k_pool, v_pool, num_tokens, num_blocks,
+                       block_size, kv_heads, head_dim);
+  if (st != PA_OK || num_tokens == 0) return st;
+  pa::WriteParams p = {};
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.slots = slot_mapping;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.num_tokens = num_tokens;
+  p.kv_heads = kv_heads;
+  p.head_dim = head_dim;
+  p.capacity = (long long)num_blocks * kBlockTokens;
+  return status_of(pa::launch_write_kv(p, static_cast<hipStream_t>(stream)));
+}
+
+int pa_write_kv_int8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                     int8_t* k_pool, int8_t* v_pool, float* k_scale, float* v_scale,
+                     int num_tokens, int num_blocks, int block_size, int kv_heads, int head_dim,
+                     void* stream) {
+  int st = check_write(k_new, v_new, slot_mapping, k_pool, v_pool, num_tokens, num_blocks,
+                       block_size, kv_heads, head_dim);
+  if (st != PA_OK) return st;
+  if (!k_scale || !v_scale) return PA_ERR_NULL;
+  if (num_tokens == 0) return PA_OK;
+  pa::WriteParams p = {};
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.slots = slot_mapping;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.num_tokens = num_tokens;
+  p.kv_heads = kv_heads;
+  p.head_dim = head_dim;
+  p.capacity = (long long)num_blocks * kBlockTokens;
+  return status_of(pa::launch_write_kv_int8(p, static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode_partition_size(int batch, int q_heads, int kv_heads, int head_dim,
+                             int max_context_len, int partition_size) {
+  if (check_decode_shapes(1 << 30 >> 4, max_context_len, batch, q_heads, kv_heads, head_dim,
+                          kBlockTokens, 1, partition_size) != PA_OK)
+    return 0;
+  return resolve_partition(batch, q_heads, kv_heads, head_dim, max_context_len, partition_size);
+}
+
+size_t pa_decode_workspace_size(int batch, int q_heads, int kv_heads, int head_dim,
+                                int max_context_len, int partition_size) {
+  const int P = pa_decode_partition_size(batch, q_heads, kv_heads, head_dim, max_context_len,
+                                         partition_size);
+  if (P == 0) return 0;
+  return record_layout(batch, q_heads, head_dim, num_partitions(max_context_len, P)).total;
+}
+
+int pa_decode(void* out, float* lse_out, const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_table, int max_blocks, const int32_t* context_lens,
+              int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
+              int block_size, int num_blocks, float scale, int partition_size, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return decode_common(0, out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_table,
+                       max_blocks, context_lens, max_context_len, batch, q_heads, kv_heads,
+                       head_dim, block_size, num_blocks, scale, partition_size, workspace,
+                       workspace_bytes, stream);
+}
+
+int pa_decode_int8(void* out, float* lse_out, const void* q, const int8_t* k_pool,
+                   const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                   const int32_t* block_table, int max_blocks, const int32_t* context_lens,
+                   int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
+                   int block_size, int num_blocks, float scale, int partition_size,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(0, out, lse_out, q, k_pool, v_pool, k_scale, v_scale, true, block_table,
+                       max_blocks, context_lens, max_context_len, batch, q_heads, kv_heads,
+                       head_dim, block_size, num_blocks, scale, partition_size, workspace,
+                       workspace_bytes, stream);
+}
+
+int pa_decode_partials(const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, int max_blocks, const int32_t* context_lens,
+                       int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
+                       int block_size, int num_blocks, float scale, int partition_size,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(1, nullptr, nullptr, q, k_pool, v_pool, nullptr, nullptr, false,
+                       block_table, max_blocks, context_lens, max_context_len, batch, q_heads,
+                       kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
+                       workspace, workspace_bytes, stream);
+}
+
+int pa_decode_partials_int8(const void* q, const int8_t* k_pool, const int8_t* v_pool,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_table, int max_blocks,
+                            const int32_t* context_lens, int max_context_len, int batch,
+                            int q_heads, int kv_heads, int head_dim, int block_size,
+                            int num_blocks, float scale, int partition_size, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_common(1, nullptr, nullptr, q, k_pool, v_pool, k_scale, v_scale, true,
+                       block_table, max_blocks, context_lens, max_context_len, batch, q_heads,
+                       kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
+                       workspace, workspace_bytes, stream);
+}
+
+int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,
+                      int max_context_len, int batch, int q_heads, int head_dim,
+                      int partition_size, const void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!out || !context_lens || !workspace) return PA_ERR_NULL;
+  if (batch < 0 || q_heads <= 0 || max_context_len < 0 || batch > 65535) return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (partition_size <= 0 || partition_size % kBlockTokens != 0 || partition_size > kMaxPartition)
+    return PA_ERR_UNSUPPORTED;
+  const int n_part = num_partitions(max_context_len, partition_size);
+  const Records rec = record_layout(batch, q_heads, head_dim, n_part);
+  if (workspace_bytes < rec.total) return PA_ERR_WORKSPACE;
+  if (batch == 0) return PA_OK;
+  pa::MergeParams mp = {};
+  mp.part_ml = static_cast<const float2*>(workspace);
+  mp.part_o = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + rec.o_offset);
+  mp.context_lens = context_lens;
+  mp.out = static_cast<uint16_t*>(out);
+  mp.lse = lse_out;
+  mp.batch = batch;
+  mp.q_heads = q_heads;
+  mp.head_dim = head_dim;
+  mp.partition_size = partition_size;
+  mp.n_part = n_part;
+  mp.max_context_len = max_context_len;
+  return status_of(pa::launch_merge(mp, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

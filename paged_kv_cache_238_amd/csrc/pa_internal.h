@@ -1,0 +1,64 @@
+// Internal interface between the C-ABI layer (pa_api.hip) and the kernel
+// launchers.  Not installed; no torch types anywhere.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlockTokens = 16;   // tokens per physical KV block
+
+// Everything one decode launch needs.  Pointers are device pointers.
+struct DecodeParams {
+  const uint16_t* q;          // fp16 [B, Hq, D]
+  const void* k_pool;         // fp16 or int8 [NB, 16, Hkv, D]
+  const void* v_pool;
+  const float* k_scale;       // int8 only: fp32 [NB, 16, Hkv]
+  const float* v_scale;
+  const int32_t* block_table; // [B, max_blocks]
+  const int32_t* context_lens;// [B]
+  uint16_t* out;              // fp16 [B, Hq, D]  (direct mode)
+  float* lse;                 // fp32 [B, Hq] or null (direct mode)
+  float2* part_ml;            // [B, Hq, n_part] (split mode)
+  float* part_o;              // [B, Hq, n_part, D] (split mode)
+  int max_blocks;
+  int max_context_len;
+  int batch, q_heads, kv_heads, head_dim, num_blocks;
+  int partition_size;         // tokens, multiple of 16
+  int n_part;                 // ceil(max_context_len / partition_size)
+  float scale_log2;           // scale * log2(e)
+  int direct;                 // 1: n_part == 1, write out/lse directly
+};
+
+struct MergeParams {
+  const float2* part_ml;
+  const float* part_o;
+  const int32_t* context_lens;
+  uint16_t* out;
+  float* lse;
+  int batch, q_heads, head_dim;
+  int partition_size, n_part, max_context_len;
+};
+
+struct WriteParams {
+  const uint16_t* k_new;      // fp16 [T, Hkv, D]
+  const uint16_t* v_new;
+  const int32_t* slots;       // [T]
+  void* k_pool;
+  void* v_pool;
+  float* k_scale;             // int8 pools only
+  float* v_scale;
+  int num_tokens, kv_heads, head_dim;
+  long long capacity;         // num_blocks * 16 slots
+};
+
+// Launchers return hipSuccess or the launch error.  `int8` selects the
+// int8-cache instantiation.
+hipError_t launch_decode(const DecodeParams& p, bool int8, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_write_kv(const WriteParams& p, hipStream_t stream);
+hipError_t launch_write_kv_int8(const WriteParams& p, hipStream_t stream);
+
+}  // namespace pa
