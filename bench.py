@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (the "
+                         "known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -220,6 +223,17 @@ def main():
               "(the decode path runs on a single device)", file=sys.stderr)
         sys.exit(2)
     import torch
+
+    if args.copy_calibration:
+        dev = torch.device("cuda:0")
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
 
     import paged_kv_cache_238_amd as pa
     from workloads import gen

@@ -24,8 +24,9 @@
  * the caller unless stated otherwise):
  *   q, out        fp16  [batch, q_heads, head_dim]
  *   k_pool,v_pool fp16 or int8 [num_blocks, block_size, kv_heads, head_dim]
- *   k_scale,      fp32  [num_blocks, block_size, kv_heads]   (int8 pools:
- *   v_scale             one scale per token and kv head)
+ *   k_scale,      fp32  [num_blocks, kv_heads, block_size]   (int8 pools:
+ *   v_scale             one scale per token and kv head; the 16 scales of
+ *                       one (block, kv head) are adjacent, one 64-byte line)
  *   block_table   int32 [batch, max_blocks]; entry j of row b is the physical
  *                       block holding logical tokens 16j .. 16j+15 of b
  *   context_lens  int32 [batch]; tokens of sequence b, including the newest
@@ -107,7 +108,7 @@ int pa_write_kv(const void* k_new, const void* v_new, const int32_t* slot_mappin
  * KVCacheQuantizer.quantize, per_channel branch (last axis = head_dim);
  * "二、优化方向" FP16 -> INT8 cache.  Same slot rules as pa_write_kv.
  *   k_pool, v_pool int8 [num_blocks, block_size, kv_heads, head_dim]
- *   k_scale, v_scale fp32 [num_blocks, block_size, kv_heads]
+ *   k_scale, v_scale fp32 [num_blocks, kv_heads, block_size]
  */
 int pa_write_kv_int8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                      int8_t* k_pool, int8_t* v_pool, float* k_scale, float* v_scale,
@@ -179,18 +180,30 @@ int pa_decode_int8(void* out, float* lse_out, const void* q, const int8_t* k_poo
  * pa_decode / pa_decode_int8 without out and lse_out; always write the
  * partition records into the workspace, which must hold
  * pa_decode_workspace_size(..., partition_size resolved, ...) bytes
- * computed with max_context_len > partition_size, i.e.
- * n_part = ceil(max_context_len / P) records per (b, h).  Record layout
+ * computed with max_context_len > partition_size, i.e. room for
+ * n_part = ceil(max_context_len / P) records per (b, h).  Workspace layout
  * (P = resolved partition size):
- *   float2 ml[batch][q_heads][n_part]   (m, l): m = max of the partition's
- *                                       scores in log2 units
- *                                       (scale * log2(e) * q.k), l = sum of
- *                                       2^(s - m)
+ *   int32  header[64]                   header[0] = span: partitions per
+ *                                       record.  Record r of (b, h) covers
+ *                                       partitions [r*span, (r+1)*span).
+ *                                       span is 1 for groups of 1 or 2; for
+ *                                       larger groups it is chosen on the
+ *                                       device from the context lengths
+ *                                       (long contexts: several partitions
+ *                                       merged online by one wave).
+ *   float2 ml[batch][q_heads][n_part]   (m, l): m = a reference point in
+ *                                       log2 units, at most the partition's
+ *                                       largest score s = scale * log2(e) *
+ *                                       q.k (and within 8 of it); l = sum of
+ *                                       2^(s - m); m + log2(l) is the
+ *                                       partition's log-sum-exp
  *   float  o[batch][q_heads][n_part][head_dim]  unnormalised sum 2^(s-m) v
- * Records of partitions at or past ceil(L_b / P) are not written.
+ *                                       (256-byte aligned after ml)
+ * Records at or past ceil(ceil(L_b / P) / span) are not written.
  *
- * pa_merge_partials: out[b,h] = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
- * over p < ceil(L_b / P), M = max m_p; lse = ln 2 * (M + log2(den)).
+ * pa_merge_partials: out[b,h] = sum_r 2^(m_r - M) o_r / sum_r 2^(m_r - M) l_r
+ * over the records r < ceil(ceil(L_b / P) / span), M = max m_r;
+ * lse = ln 2 * (M + log2(den)).
  */
 int pa_decode_partials(const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, int max_blocks,

@@ -39,8 +39,8 @@ def brute_decode(q, k_pool, v_pool, block_table, context_lens, scale,
             scores, vals = [], []
             for t in range(L):
                 blk, off = logical_to_physical(block_table[b], t)
-                ks = float(k_scale[blk][off][g]) if k_scale is not None else 1.0
-                vs = float(v_scale[blk][off][g]) if v_scale is not None else 1.0
+                ks = float(k_scale[blk][g][off]) if k_scale is not None else 1.0
+                vs = float(v_scale[blk][g][off]) if v_scale is not None else 1.0
                 acc = 0.0
                 for d in range(D):
                     acc += float(q[b][h][d]) * (float(k_pool[blk][off][g][d]) * ks)

@@ -74,7 +74,7 @@ def gather_sequence(pool: np.ndarray, table_row: np.ndarray, length: int,
         n = min(TOKENS_PER_BLOCK, L - j * TOKENS_PER_BLOCK)
         rows = pool[phys, :n, kv_head, :].astype(np.float64)
         if scale_pool is not None:
-            rows = rows * scale_pool[phys, :n, kv_head].astype(np.float64)[:, None]
+            rows = rows * scale_pool[phys, kv_head, :n].astype(np.float64)[:, None]
         dense[j * TOKENS_PER_BLOCK:j * TOKENS_PER_BLOCK + n] = rows
     return dense
 
@@ -114,7 +114,8 @@ def ref_decode(q, k_pool, v_pool, block_table, context_lens, scale,
     """Decode attention for one query token per sequence.
 
     q [B, Hq, D] fp16; k_pool / v_pool [NB, 16, Hkv, D] fp16 or int8;
-    k_scale / v_scale [NB, 16, Hkv] fp32 for int8 pools; block_table
+    k_scale / v_scale [NB, Hkv, 16] fp32 for int8 pools (one scale per token
+    and kv head, the 16 slots of a (block, kv head) adjacent); block_table
     [B, max_blocks]; context_lens [B] (including the newest token).
     rows: optional iterable of (b, h) to evaluate; the others stay NaN.
     Returns out fp64 [B, Hq, D] and lse fp64 [B, Hq] (natural log)."""

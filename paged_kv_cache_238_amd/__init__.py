@@ -152,7 +152,7 @@ def write_kv_int8(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale) 
     _need(slot_mapping, "slot_mapping", torch.int32, 1, dev)
     NB, bs, Hkv, D = k_pool.shape
     T = k_new.shape[0]
-    if v_pool.shape != k_pool.shape or k_scale.shape != (NB, bs, Hkv) \
+    if v_pool.shape != k_pool.shape or k_scale.shape != (NB, Hkv, bs) \
             or v_scale.shape != k_scale.shape or k_new.shape != (T, Hkv, D) \
             or v_new.shape != k_new.shape or slot_mapping.shape[0] != T:
         raise ValueError("write_kv_int8: inconsistent shapes")
@@ -191,8 +191,8 @@ def _decode_args(q, k_pool, v_pool, block_table, context_lens, kv_dtype, max_con
     if k_scale is not None:
         _need(k_scale, "k_scale", torch.float32, 3, dev)
         _need(v_scale, "v_scale", torch.float32, 3, dev)
-        if k_scale.shape != (NB, bs, Hkv) or v_scale.shape != k_scale.shape:
-            raise ValueError("decode_int8: scale shapes must be [num_blocks, block_size, kv_heads]")
+        if k_scale.shape != (NB, Hkv, bs) or v_scale.shape != k_scale.shape:
+            raise ValueError("decode_int8: scale shapes must be [num_blocks, kv_heads, block_size]")
     if max_context_len is None:
         # host bound from the device lengths (one synchronising read); pass it
         # explicitly to avoid the read

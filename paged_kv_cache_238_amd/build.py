@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.hip", "decode.hip", "merge.hip", "write_kv.hip"]
+SOURCES = ["pa_api.hip", "decode.hip", "decode_mfma.hip", "merge.hip", "write_kv.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -1,4 +1,6 @@
-// Paged-attention decode, split-K partition kernel (VALU form) for gfx950.
+// Paged-attention decode, split-K partition kernel (VALU form) for gfx950,
+// used for query-head groups of 1 or 2 (larger groups use the matrix-core
+// kernel in decode_mfma.hip).
 //
 // One workgroup = one (partition, kv head, sequence).  Its four wave64s walk
 // the partition's 16-token blocks (wave w takes blocks w, w+4, ...), each
@@ -118,13 +120,19 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   constexpr int ESZ = I8 ? 1 : 2;
   extern __shared__ float smem[];
 
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // 1-D grid, partition slowest (see the matrix-core kernel): consecutive
+  // workgroups, which land on different XCDs, are different (sequence, kv
+  // head) pairs of one partition index.
+  const int pairs = p.batch * p.kv_heads;
+  const int part = blockIdx.x / pairs;
+  const int b = (blockIdx.x % pairs) / p.kv_heads, g = (blockIdx.x % pairs) % p.kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int r = lane / LPR, c = lane % LPR;
   const int Hq = p.q_heads, Hkv = p.kv_heads;
   const int h0 = g * G;
 
+  if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = 1;   // one partition per record
   const int L = p.context_lens[b];
   const int P = p.partition_size;
   const int t_begin = part * P;
@@ -196,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     lane_off[i] = ((uint32_t)(r + RPW * i) * Hkv * D + (uint32_t)g * D + (uint32_t)c * 8) * ESZ;
   uint32_t scale_off[NL];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) scale_off[i] = (uint32_t)(r + RPW * i) * Hkv + g;
+  for (int i = 0; i < NL; ++i) scale_off[i] = (uint32_t)g * kBlockTokens + r + RPW * i;   // [NB, Hkv, 16]
   const char* kbase = static_cast<const char*>(p.k_pool);
   const char* vbase = static_cast<const char*>(p.v_pool);
 
@@ -417,8 +425,8 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   const size_t lds_ids = (size_t)max_ids * sizeof(int);
   const size_t lds_merge = (size_t)kWaves * G * (D + 2) * sizeof(float) + kWaves * sizeof(int);
   const size_t lds = lds_ids > lds_merge ? lds_ids : lds_merge;
-  dim3 grid(p.n_part, p.kv_heads, p.batch);
-  hipLaunchKernelGGL((decode_valu_kernel<D, G, I8>), grid, dim3(kThreads), lds, stream, p);
+  const unsigned grid = (unsigned)p.n_part * p.batch * p.kv_heads;
+  hipLaunchKernelGGL((decode_valu_kernel<D, G, I8>), dim3(grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -427,19 +435,22 @@ hipError_t dispatch_group(const DecodeParams& p, hipStream_t stream) {
   switch (p.q_heads / p.kv_heads) {
     case 1: return launch_one<D, 1, I8>(p, stream);
     case 2: return launch_one<D, 2, I8>(p, stream);
-    case 4: return launch_one<D, 4, I8>(p, stream);
-    case 8: return launch_one<D, 8, I8>(p, stream);
-    case 16: return launch_one<D, 16, I8>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, bool int8, hipStream_t stream) {
+hipError_t launch_decode_valu(const DecodeParams& p, bool int8, hipStream_t stream) {
   if (p.head_dim == 128) return int8 ? dispatch_group<128, true>(p, stream) : dispatch_group<128, false>(p, stream);
   if (p.head_dim == 64) return int8 ? dispatch_group<64, true>(p, stream) : dispatch_group<64, false>(p, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeParams& p, bool int8, hipStream_t stream) {
+  const int group = p.q_heads / p.kv_heads;
+  if (group >= 4) return launch_decode_mfma(p, int8, stream);
+  return launch_decode_valu(p, int8, stream);
 }
 
 }  // namespace pa

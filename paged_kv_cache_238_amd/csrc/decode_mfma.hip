@@ -1,0 +1,516 @@
+// Paged-attention decode, split-K partition kernel for grouped query heads
+// (G = q_heads / kv_heads in {4, 8, 16}) on gfx950 matrix cores.
+//
+// With G query heads sharing one kv head, each K/V row is used G times, so
+// the dot products and the V accumulation form real tiles:
+//   S^T[t][h] = sum_d K[t][d] Q[h][d]     16 tokens x 16 heads, k = head_dim
+//   O^T[d][h] += sum_t V[t][d] P[h][t]    16 dims  x 16 heads, k = 16 tokens
+// Heads are padded to 16 (rows h >= G hold zeros and are never stored).
+// The first product takes K straight from the global loads as the A operand
+// of v_mfma_f32_16x16x32_f16 (a lane holds 8 elements of one token row).  In
+// the result every lane owns one head (lane % 16) and four tokens, so the
+// online softmax needs only one cross-row max per block.  The second product
+// needs V with tokens along the contraction; V is staged in LDS in its
+// natural [token][dim] order and read back transposed with ds_read_b64_tr_b16,
+// and the probabilities already sit in the B-operand layout of
+// v_mfma_f32_16x16x16_f16.  O^T keeps the head on lane % 16, so the
+// per-head rescale by the running-max correction is a per-lane multiply.
+//
+// int8 caches: codes are converted exactly to fp16 (0x6400 | (x ^ 0x80) is
+// 1152 + x; subtracting 1152 in packed fp16 leaves x), the per-token K scale
+// is applied to the score and the V scale to the probability.
+//
+// Method and readings are those of the VALU kernel (zskr.cn ATB
+// PagedAttention article, section "PagedAttention 的 Attention 计算修改",
+// with the running max updated before the exponent, -inf start, a scale,
+// fp32 accumulation, per-head output and masked tail slots; the page table
+// staged on chip once per workgroup, section "踩坑一"; query heads grouped on
+// one K/V head, discosf.com article, section "二、优化方向").
+#include "pa_internal.h"
+#include "run_span.h"
+
+#include <type_traits>
+
+namespace pa {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;   // at most four waves (kv heads) per workgroup
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.693147180559945309f;
+#ifndef PA_V_ROW_PAD
+#define PA_V_ROW_PAD 16
+#endif
+constexpr int kRowPad = PA_V_ROW_PAD;   // bytes of padding per LDS row of the V tile
+// The running max is only moved (and the accumulators rescaled) when a block
+// beats it by more than this many log2 units; softmax is invariant to the
+// reference point, and probabilities stay <= 2^8, well inside fp16.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  _Float16 h = (_Float16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Four int8 codes -> four exact fp16 values.
+__device__ __forceinline__ void i8x4_to_h4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;                          // x + 128 as unsigned bytes
+  lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);     // halves 0x64xx: 1024 + byte
+  hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const h2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lo) + off);
+  hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, hi) + off);
+}
+
+// Four int8 codes -> four fp16 values 1152 + x (exact; the bias is removed
+// from the dot product as 1152 * sum(q) instead of per element).
+__device__ __forceinline__ void i8x4_to_h4_biased(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+}
+
+__device__ __forceinline__ void i8x16_to_h16_biased(const uint4& c, uint4& first, uint4& second) {
+  i8x4_to_h4_biased(c.x, first.x, first.y);
+  i8x4_to_h4_biased(c.y, first.z, first.w);
+  i8x4_to_h4_biased(c.z, second.x, second.y);
+  i8x4_to_h4_biased(c.w, second.z, second.w);
+}
+
+// 16 int8 codes -> 16 fp16 (two 8-element halves).
+__device__ __forceinline__ void i8x16_to_h16(const uint4& c, uint4& first, uint4& second) {
+  i8x4_to_h4(c.x, first.x, first.y);
+  i8x4_to_h4(c.y, first.z, first.w);
+  i8x4_to_h4(c.z, second.x, second.y);
+  i8x4_to_h4(c.w, second.z, second.w);
+}
+
+template <int D, bool I8>
+struct Geometry {
+  // 16-byte global loads per lane per block for K (and again for V).
+  static constexpr int kLoads = I8 ? D / 64 : D / 32;
+  // QK MFMA steps (8 dims of k per lane each).
+  static constexpr int kSteps = D / 32;
+  // Head-dim index held by lane group g, element j of QK step kk.
+  static __device__ __forceinline__ int dim(int kk, int g, int j) {
+    if constexpr (I8) return 64 * (kk / 2) + 16 * g + 8 * (kk % 2) + j;
+    else return 32 * kk + 8 * g + j;
+  }
+  // Byte offset, within a token row of D elements, of load `ld` of group g.
+  static __device__ __forceinline__ uint32_t load_off(int ld, int g) {
+    if constexpr (I8) return (uint32_t)(64 * ld + 16 * g);
+    else return (uint32_t)(64 * ld + 16 * g);   // 32*ld + 8*g elements of 2 bytes
+  }
+  static constexpr int kRowBytes = D * 2 + kRowPad;   // LDS row of the fp16 V tile
+};
+
+// Three waves per SIMD (<= 168 registers): memory-level parallelism is what
+// bounds this kernel, so occupancy is worth more than deeper unrolling.
+//
+// Work split: a workgroup holds `wpg` waves (1, 2 or 4) for wpg consecutive
+// kv heads of one (sequence, partition); each wave streams its own head's
+// whole partition and writes its own record.  The waves of a workgroup thus
+// read neighbouring slices of the same token rows at the same time, and a
+// wave's start-up (length, block ids, Q) is paid once per partition.
+template <int D, int G, bool I8>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_mfma_kernel(const DecodeParams p) {
+  using Geo = Geometry<D, I8>;
+  constexpr int NLD = Geo::kLoads;
+  constexpr int NKK = Geo::kSteps;
+  constexpr int NT = D / 16;                 // O^T tiles of 16 dims
+  constexpr int ESZ = I8 ? 1 : 2;
+  constexpr int TILE = kBlockTokens * Geo::kRowBytes;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wpg = blockDim.x >> 6;           // kv heads per workgroup
+  const int lg = lane >> 4;       // lane group 0..3
+  const int li = lane & 15;       // index in group: token row for loads, head for softmax
+  const int Hq = p.q_heads, Hkv = p.kv_heads;
+
+  // 1-D grid, run index slowest: consecutive workgroups (dealt round-robin
+  // to the eight XCDs) are the head groups and sequences of one run index,
+  // so every XCD gets an even share even when lengths differ.  A wave
+  // streams run `ridx` (partitions [ridx*span, (ridx+1)*span)) of its head
+  // and merges it online into one record.
+  const int groups = Hkv / wpg;
+  const int per_run = p.batch * groups;
+  const int ridx = blockIdx.x / per_run;
+  const int rem = blockIdx.x % per_run;
+  const int b = rem / groups;
+  const int g = (rem % groups) * wpg + w;
+  const int h0 = g * G;
+
+  const int P = p.partition_size;
+  const int span = p.direct ? 1 : run_span(p.context_lens, p.batch, Hkv, p.max_context_len, P,
+                                           p.target_waves);
+  if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = span;
+  const int part0 = ridx * span;             // first partition of this run
+  const int t_begin = part0 * P;
+  const int j0 = min(t_begin / kBlockTokens, p.max_blocks - 1);
+  const int32_t* bt_row = p.block_table + (size_t)b * p.max_blocks;
+
+  // Start-up loads, all independent: the length, the first 64 block ids of
+  // the run (clamped to the table row; only those below the length are
+  // used) and Q.  Block ids live one per lane and are read back with
+  // v_readlane, so the table slice is fetched once per wave.
+  const int L = p.context_lens[b];
+  const int row_left = p.max_blocks - j0;
+  const int span_blocks = span * (P / kBlockTokens);
+  auto load_ids = [&](int c0) {              // block ids c0 .. c0+63 of the span
+    const int cnt = min(min(span_blocks, row_left) - c0, 64);
+    return (lane < cnt) ? bt_row[j0 + c0 + lane] : 0;
+  };
+  int ids = load_ids(0);
+
+  // Q^T as the B operand of the QK product: lane holds Q[h0 + li][dim(kk, lg, j)].
+  // Each step's 8 dims are consecutive (Geo::dim), so one 16-byte load each;
+  // padding heads (li >= G) load head 0 and are zeroed.
+  h8 qB[NKK];
+  {
+    const bool real_head = li < G;
+    const uint16_t* qrow = p.q + ((size_t)b * Hq + h0 + (real_head ? li : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + Geo::dim(kk, lg, 0));
+      if (!real_head) v = make_uint4(0, 0, 0, 0);
+      qB[kk] = __builtin_bit_cast(h8, v);
+    }
+  }
+
+  if (L < 0 || L > p.max_context_len) {      // broken metadata: NaN rows
+    if (ridx == 0 && p.direct && li < G) {
+      const size_t row = (size_t)b * Hq + h0 + li;
+      for (int d = lg; d < D; d += 4) p.out[row * D + d] = 0x7E00;
+      if (lg == 0 && p.lse) p.lse[row] = __builtin_nanf("");
+    }
+    return;
+  }
+  if (t_begin >= L) {                        // empty run (L == 0: zero row)
+    if (p.direct && ridx == 0 && li < G) {
+      const size_t row = (size_t)b * Hq + h0 + li;
+      for (int d = lg; d < D; d += 4) p.out[row * D + d] = 0;
+      if (lg == 0 && p.lse) p.lse[row] = kNegInf;
+    }
+    return;
+  }
+  const int ntok = min(t_begin + span_blocks * kBlockTokens, L) - t_begin;
+  const int nfull = ntok / kBlockTokens;
+  const int tail = ntok - nfull * kBlockTokens;
+
+  char* s_tile = smem + w * TILE;            // this wave's V tile
+
+  // int8: sum over head_dim of q for head li (removes the 1152 bias of K).
+  float qbias = 0.f;
+  if constexpr (I8) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qbias += (float)qB[kk][j];
+    }
+    qbias += __shfl_xor(qbias, 16);
+    qbias += __shfl_xor(qbias, 32);
+    qbias *= 1152.0f;
+  }
+
+  f4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf;   // reference max of head li (same in all four lane groups)
+  float l_run = 0.f;       // this lane's share of the running sum (its tokens)
+  bool bad_blk = false;
+
+  const uint32_t row_bytes = (uint32_t)Hkv * D * ESZ;          // one token row, all heads
+  const uint32_t blk_bytes = (uint32_t)kBlockTokens * row_bytes;
+  const uint32_t lane_row_off = (uint32_t)li * row_bytes + (uint32_t)g * D * ESZ;
+  const char* kbase = static_cast<const char*>(p.k_pool);
+  const char* vbase = static_cast<const char*>(p.v_pool);
+  const uint32_t scale_blk_bytes = (uint32_t)kBlockTokens * Hkv * sizeof(float);
+
+  // LDS addresses of this lane's transposed V reads: tile nb, group lg reads
+  // token rows 4*lg + li/4 at dims 16*nb + 4*(li%4) (8 bytes each).
+  const uint32_t tr_base = (uint32_t)(4 * lg + li / 4) * Geo::kRowBytes + (uint32_t)(4 * (li % 4)) * 2;
+
+  struct Regs {
+    uint4 k[NLD];
+    uint4 v[NLD];
+    f4 ks;          // int8: scales of this lane's softmax tokens 4*lg .. 4*lg+3
+    f4 vs;
+  };
+
+  // Loads of one block.  real == false: a prefetch past the end; its
+  // resource is empty, so the loads return zeros without touching memory.
+  auto load_block = [&](int blk, bool real, Regs& R) {
+    if ((unsigned)blk >= (unsigned)p.num_blocks) {
+      if (real) bad_blk = true;              // the record becomes NaN
+      real = false;
+      blk = 0;
+    }
+    const uint32_t nbytes = real ? blk_bytes : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)blk * blk_bytes, nbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)blk * blk_bytes, nbytes);
+#pragma unroll
+    for (int ld = 0; ld < NLD; ++ld) R.k[ld] = buffer_load16(rk, lane_row_off + Geo::load_off(ld, lg));
+#pragma unroll
+    for (int ld = 0; ld < NLD; ++ld) R.v[ld] = buffer_load16(rv, lane_row_off + Geo::load_off(ld, lg));
+    if constexpr (I8) {
+      // scales [NB, Hkv, 16]: this lane's four softmax tokens 4*lg .. 4*lg+3
+      // of kv head g are one 16-byte load
+      const uint32_t sbytes = real ? scale_blk_bytes : 0u;
+      const size_t sblk = (size_t)blk * kBlockTokens * Hkv;
+      const uint32_t soff = ((uint32_t)g * kBlockTokens + 4 * lg) * 4u;
+      R.ks = __builtin_bit_cast(f4, buffer_load16(make_rsrc(p.k_scale + sblk, sbytes), soff));
+      R.vs = __builtin_bit_cast(f4, buffer_load16(make_rsrc(p.v_scale + sblk, sbytes), soff));
+    }
+  };
+  auto process_block = [&](auto tail_tag, const Regs& R, int valid) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    // K as fp16 A operands, one per QK step.
+    h8 kA[NKK];
+    if constexpr (I8) {
+#pragma unroll
+      for (int ld = 0; ld < NLD; ++ld) {
+        uint4 a, c;
+        i8x16_to_h16_biased(R.k[ld], a, c);
+        kA[2 * ld] = __builtin_bit_cast(h8, a);
+        kA[2 * ld + 1] = __builtin_bit_cast(h8, c);
+      }
+    } else {
+#pragma unroll
+      for (int ld = 0; ld < NLD; ++ld) kA[ld] = __builtin_bit_cast(h8, R.k[ld]);
+    }
+    f4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qB[kk], s, 0, 0, 0);
+
+    // V into this wave's LDS tile, natural [token][dim] order (fp16).
+    {
+      const bool zero_row = TAIL && li >= valid;   // tail slot: may hold NaN
+      char* rowp = s_tile + li * Geo::kRowBytes;
+      if constexpr (I8) {
+#pragma unroll
+        for (int ld = 0; ld < NLD; ++ld) {
+          uint4 a, c;
+          i8x16_to_h16(R.v[ld], a, c);
+          if (zero_row) a = c = make_uint4(0, 0, 0, 0);
+          const int d0 = 64 * ld + 16 * lg;
+          *reinterpret_cast<uint4*>(rowp + d0 * 2) = a;
+          *reinterpret_cast<uint4*>(rowp + d0 * 2 + 16) = c;
+        }
+      } else {
+#pragma unroll
+        for (int ld = 0; ld < NLD; ++ld) {
+          uint4 a = R.v[ld];
+          if (zero_row) a = make_uint4(0, 0, 0, 0);
+          const int d0 = 32 * ld + 8 * lg;
+          *reinterpret_cast<uint4*>(rowp + d0 * 2) = a;
+        }
+      }
+    }
+
+    // Online softmax of head li over tokens 4*lg + i.
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x;
+      if constexpr (I8) x = (s[i] - qbias) * (p.scale_log2 * R.ks[i]);
+      else x = s[i] * p.scale_log2;
+      if constexpr (TAIL) {
+        if (4 * lg + i >= valid) x = kNegInf;
+      }
+      sc[i] = x;
+    }
+    float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    // Move the reference max only when some head of the wave outgrows it.
+    if (__builtin_amdgcn_ballot_w64(mb > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mb);
+      const float alpha = fast_exp2(m_run - ((m_new == kNegInf) ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - m_use);
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    h4 pB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float pv = pr[i];
+      if constexpr (I8) {
+        float vsc = R.vs[i];
+        if constexpr (TAIL) {
+          if (4 * lg + i >= valid) vsc = 0.f;
+        }
+        pv *= vsc;
+      }
+      pB[i] = (_Float16)pv;
+    }
+
+    // O^T += V^T P^T, V^T read transposed from LDS.
+    typedef __attribute__((address_space(3))) s4 lds_s4;
+    const __attribute__((address_space(3))) char* tile3 =
+        (const __attribute__((address_space(3))) char*)(s_tile);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(tile3 + tr_base + n * 32));
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, a), pB, acc[n], 0,
+                                                     0, 0);
+    }
+  };
+
+  // Record of the run (relative to m_run).
+  // Lane (lg, li) holds O[head li][dim 16n + 4lg + i].
+  auto finalize = [&]() {
+    float den = l_run;
+    den += __shfl_xor(den, 16);
+    den += __shfl_xor(den, 32);
+    if (li < G) {
+      const size_t row = (size_t)b * Hq + h0 + li;
+      float M = m_run;
+      if (bad_blk) M = den = __builtin_nanf("");
+      if (p.direct) {
+        const float inv = 1.0f / den;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          uint2 o;
+          o.x = (uint32_t)f32_to_f16_bits(acc[n][0] * inv) |
+                ((uint32_t)f32_to_f16_bits(acc[n][1] * inv) << 16);
+          o.y = (uint32_t)f32_to_f16_bits(acc[n][2] * inv) |
+                ((uint32_t)f32_to_f16_bits(acc[n][3] * inv) << 16);
+          if (bad_blk) o = make_uint2(0x7E007E00u, 0x7E007E00u);
+          *reinterpret_cast<uint2*>(p.out + row * D + 16 * n + 4 * lg) = o;
+        }
+        if (lg == 0 && p.lse) p.lse[row] = (M + log2f(den)) * kLn2;
+      } else {
+        const size_t rec = row * p.n_part + ridx;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          f4 o = acc[n];
+          if (bad_blk) o = f4{M, M, M, M};
+          *reinterpret_cast<f4*>(p.part_o + rec * D + 16 * n + 4 * lg) = o;
+        }
+        if (lg == 0) p.part_ml[rec] = make_float2(M, den);
+      }
+    }
+  };
+
+  // Full blocks of the span, streamed in order.  Block ids come one per
+  // lane from a 64-block chunk (the next chunk's ids are fetched when a
+  // chunk starts).  Register sets rotate so that NBUF - 1 blocks are in
+  // flight while one is reduced (int8 blocks are half the bytes, so they go
+  // one deeper); prefetches past the end read nothing.  Every branch is
+  // wave-uniform and no load sits inside one, so the waits stay exact.
+  std::integral_constant<bool, false> full;
+  int ids_next = load_ids(64);
+  int id_chunk = 0;                          // chunk held in `ids`
+  auto issue = [&](int k, Regs& R) {
+    const bool real = k < nfull;
+    const int kk = real ? k : 0;
+    const int src = (kk >> 6) == id_chunk ? ids : ids_next;
+    load_block(__builtin_amdgcn_readlane(src, kk & 63), real, R);
+  };
+  auto done = [&](int k) {                   // block k reduced
+    if (((k + 1) & 63) == 0) {               // leave chunk k >> 6
+      ids = ids_next;
+      ++id_chunk;
+      ids_next = load_ids((id_chunk + 1) * 64);
+    }
+  };
+  if (nfull > 0) {
+    if constexpr (I8) {
+      Regs A, B, C;
+      issue(0, A);
+      issue(1, B);
+      for (int k = 0; k < nfull; k += 3) {
+        issue(k + 2, C);
+        __builtin_amdgcn_sched_barrier(0);
+        process_block(full, A, kBlockTokens);
+        done(k);
+        issue(k + 3, A);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 1 < nfull) { process_block(full, B, kBlockTokens); done(k + 1); }
+        issue(k + 4, B);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 2 < nfull) { process_block(full, C, kBlockTokens); done(k + 2); }
+      }
+    } else {
+      Regs A, B;
+      issue(0, A);
+      for (int k = 0; k < nfull; k += 2) {
+        issue(k + 1, B);
+        __builtin_amdgcn_sched_barrier(0);
+        process_block(full, A, kBlockTokens);
+        done(k);
+        issue(k + 2, A);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 1 < nfull) { process_block(full, B, kBlockTokens); done(k + 1); }
+      }
+    }
+  }
+  // The partial last block (only in a sequence's last partition).
+  if (tail > 0) {
+    Regs T;
+    load_block(bt_row[j0 + nfull], true, T);
+    process_block(std::integral_constant<bool, true>(), T, tail);
+  }
+  finalize();
+}
+
+template <int D, int G, bool I8>
+hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
+  using Geo = Geometry<D, I8>;
+  const int wpg = (p.kv_heads % 4 == 0) ? 4 : (p.kv_heads % 2 == 0) ? 2 : 1;
+  const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes;
+  // runs never outnumber partitions, so n_part bounds the run index
+  const unsigned grid = (unsigned)p.n_part * p.batch * (p.kv_heads / wpg);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G, I8>), dim3(grid), dim3(64 * wpg), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool I8>
+hipError_t dispatch_group(const DecodeParams& p, hipStream_t stream) {
+  switch (p.q_heads / p.kv_heads) {
+    case 4: return launch_one<D, 4, I8>(p, stream);
+    case 8: return launch_one<D, 8, I8>(p, stream);
+    case 16: return launch_one<D, 16, I8>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeParams& p, bool int8, hipStream_t stream) {
+  if (p.head_dim == 128)
+    return int8 ? dispatch_group<128, true>(p, stream) : dispatch_group<128, false>(p, stream);
+  if (p.head_dim == 64)
+    return int8 ? dispatch_group<64, true>(p, stream) : dispatch_group<64, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,8 +1,9 @@
 // Log-sum-exp merge of split-K partition records into the final fp16 row.
 //
-// Partition p of sequence b, query head h carries (m_p, l_p, o_p): the max
-// score of its tokens (log2 units), sum of 2^(s - m_p) and the unnormalised
-// sum of 2^(s - m_p) v.  With M = max_p m_p and w_p = 2^(m_p - M):
+// Record r of sequence b, query head h carries (m_r, l_r, o_r) for a run of
+// `span` consecutive partitions (span from the workspace header): a
+// reference point m_r for its scores (log2 units), the sum of 2^(s - m_r)
+// and the unnormalised sum of 2^(s - m_r) v.  With M = max_p m_p and w_p = 2^(m_p - M):
 //   out = sum_p w_p o_p / sum_p w_p l_p,   lse = ln2 * (M + log2 sum_p w_p l_p).
 // This is the running-max rescaling of the zskr.cn article's PagedAttention
 // kernel (section "PagedAttention 的 Attention 计算修改") applied once
@@ -45,7 +46,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
     if (tid == 0 && p.lse) p.lse[row] = __builtin_nanf("");
     return;
   }
-  const int n = (L + p.partition_size - 1) / p.partition_size;
+  // records cover runs of `span` partitions (written by the partition kernel)
+  const int span = max(1, p.header[0]);
+  const int n_part_b = (L + p.partition_size - 1) / p.partition_size;
+  const int n = (n_part_b + span - 1) / span;
   if (n == 0) {
     for (int d = tid; d < D; d += kThreads) p.out[row * D + d] = 0;
     if (tid == 0 && p.lse) p.lse[row] = kNegInf;

@@ -10,7 +10,13 @@ namespace {
 
 using pa::kBlockTokens;
 
-constexpr int kDefaultPartition = 512;      // tokens per split-K partition
+constexpr int kDefaultPartition = 512;      // smallest automatic partition (tokens)
+constexpr int kMatrixPartition = 256;       // matrix-core kernel's split granularity
+constexpr int kMaxAutoPartition = 4096;     // largest automatic partition
+constexpr long long kMinWorkgroups = 2048;  // 256 CUs x 8
+// Matrix-core kernel: runs are lengthened while at least this many remain
+// (256 CUs x 8 waves, two four-wave workgroups per CU).
+constexpr long long kTargetWaves = 2048;
 constexpr int kMaxPartition = 1 << 18;      // block ids of one partition fit LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -36,11 +42,24 @@ int check_decode_shapes(int max_blocks, int max_context_len, int batch, int q_he
   return PA_OK;
 }
 
+// Library's partition size.  Matrix-core kernel (groups of 4+): 256 tokens;
+// it merges runs of partitions per wave, sized on the device from the
+// actual lengths, so the partition only sets the finest split.  VALU kernel: start at 512 tokens and double
+// (up to 4096) while the grid would still hold at least kMinWorkgroups
+// workgroups; a partition there costs a fixed prologue (block ids, Q) and
+// epilogue (cross-wave merge, record store), so larger partitions win as
+// long as every CU keeps several workgroups.
 int resolve_partition(int batch, int q_heads, int kv_heads, int head_dim, int max_context_len,
                       int partition_size) {
-  (void)batch; (void)q_heads; (void)kv_heads; (void)head_dim; (void)max_context_len;
+  (void)head_dim;
   if (partition_size > 0) return partition_size;
-  return kDefaultPartition;
+  if (kv_heads > 0 && q_heads / kv_heads >= 4) return kMatrixPartition;
+  const long long pairs = (long long)batch * kv_heads;
+  int P = kDefaultPartition;
+  while (P < kMaxAutoPartition &&
+         pairs * ((max_context_len + 2LL * P - 1) / (2LL * P)) >= kMinWorkgroups)
+    P *= 2;
+  return P;
 }
 
 int num_partitions(int max_context_len, int P) {
@@ -48,15 +67,18 @@ int num_partitions(int max_context_len, int P) {
   return n > 0 ? n : 1;
 }
 
+// Workspace: [header, 256 B: int32 run span][(m, l) records][o records].
 struct Records {
-  size_t ml_bytes, o_offset, total;
+  size_t ml_offset, o_offset, total;
 };
+
+constexpr size_t kHeaderBytes = 256;
 
 Records record_layout(int batch, int q_heads, int head_dim, int n_part) {
   Records r;
   const size_t n = (size_t)batch * q_heads * n_part;
-  r.ml_bytes = n * sizeof(float2);
-  r.o_offset = align_up(r.ml_bytes, 256);
+  r.ml_offset = kHeaderBytes;
+  r.o_offset = align_up(r.ml_offset + n * sizeof(float2), 256);
   r.total = r.o_offset + n * head_dim * sizeof(float);
   return r;
 }
@@ -80,6 +102,7 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   const int P = resolve_partition(batch, q_heads, kv_heads, head_dim, max_context_len,
                                   partition_size);
   const int n_part = num_partitions(max_context_len, P);
+  if ((long long)n_part * batch * kv_heads > INT_MAX) return PA_ERR_SHAPE;   // 1-D grids
   const bool direct = (mode == 0 && n_part == 1);
   const Records rec = record_layout(batch, q_heads, head_dim, n_part);
   if (!direct) {
@@ -98,9 +121,10 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   p.context_lens = context_lens;
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse_out;
-  p.part_ml = direct ? nullptr : static_cast<float2*>(workspace);
-  p.part_o = direct ? nullptr
-                    : reinterpret_cast<float*>(static_cast<char*>(workspace) + rec.o_offset);
+  char* ws = static_cast<char*>(workspace);
+  p.header = direct ? nullptr : reinterpret_cast<int*>(ws);
+  p.part_ml = direct ? nullptr : reinterpret_cast<float2*>(ws + rec.ml_offset);
+  p.part_o = direct ? nullptr : reinterpret_cast<float*>(ws + rec.o_offset);
   p.max_blocks = max_blocks;
   p.max_context_len = max_context_len;
   p.batch = batch;
@@ -112,11 +136,13 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   p.n_part = n_part;
   p.scale_log2 = scale * kLog2e;
   p.direct = direct ? 1 : 0;
+  p.target_waves = (int)kTargetWaves;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = status_of(pa::launch_decode(p, int8, s));
   if (st != PA_OK || direct || mode == 1) return st;
 
   pa::MergeParams mp = {};
+  mp.header = p.header;
   mp.part_ml = p.part_ml;
   mp.part_o = p.part_o;
   mp.context_lens = context_lens;
@@ -280,8 +306,10 @@ int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,
   if (workspace_bytes < rec.total) return PA_ERR_WORKSPACE;
   if (batch == 0) return PA_OK;
   pa::MergeParams mp = {};
-  mp.part_ml = static_cast<const float2*>(workspace);
-  mp.part_o = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + rec.o_offset);
+  const char* ws = static_cast<const char*>(workspace);
+  mp.header = reinterpret_cast<const int*>(ws);
+  mp.part_ml = reinterpret_cast<const float2*>(ws + rec.ml_offset);
+  mp.part_o = reinterpret_cast<const float*>(ws + rec.o_offset);
   mp.context_lens = context_lens;
   mp.out = static_cast<uint16_t*>(out);
   mp.lse = lse_out;

@@ -15,7 +15,7 @@ struct DecodeParams {
   const uint16_t* q;          // fp16 [B, Hq, D]
   const void* k_pool;         // fp16 or int8 [NB, 16, Hkv, D]
   const void* v_pool;
-  const float* k_scale;       // int8 only: fp32 [NB, 16, Hkv]
+  const float* k_scale;       // int8 only: fp32 [NB, Hkv, 16]
   const float* v_scale;
   const int32_t* block_table; // [B, max_blocks]
   const int32_t* context_lens;// [B]
@@ -30,9 +30,12 @@ struct DecodeParams {
   int n_part;                 // ceil(max_context_len / partition_size)
   float scale_log2;           // scale * log2(e)
   int direct;                 // 1: n_part == 1, write out/lse directly
+  int target_waves;           // matrix-core kernel: run-length target (run_span.h)
+  int* header;                // split mode: workspace header; [0] = run span
 };
 
 struct MergeParams {
+  const int* header;          // [0] = partitions per record (run span)
   const float2* part_ml;
   const float* part_o;
   const int32_t* context_lens;
@@ -56,7 +59,10 @@ struct WriteParams {
 
 // Launchers return hipSuccess or the launch error.  `int8` selects the
 // int8-cache instantiation.
+// Group size 1 or 2: VALU kernel; 4, 8 or 16: matrix-core kernel.
 hipError_t launch_decode(const DecodeParams& p, bool int8, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeParams& p, bool int8, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, bool int8, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_write_kv(const WriteParams& p, hipStream_t stream);
 hipError_t launch_write_kv_int8(const WriteParams& p, hipStream_t stream);

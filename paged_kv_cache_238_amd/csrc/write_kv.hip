@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(const WriteParams
   if (slot < 0 || (long long)slot >= p.capacity) return;
   const size_t src = ((size_t)tok * p.kv_heads + g) * D;
   const size_t dst = ((size_t)slot * p.kv_heads + g) * D;
-  const size_t sdst = (size_t)slot * p.kv_heads + g;
+  const size_t sdst = ((size_t)(slot / 16) * p.kv_heads + g) * 16 + slot % 16;   // [NB, Hkv, 16]
   quantise_row<D>(p.k_new + src, static_cast<int8_t*>(p.k_pool) + dst, p.k_scale + sdst, lane);
   quantise_row<D>(p.v_new + src, static_cast<int8_t*>(p.v_pool) + dst, p.v_scale + sdst, lane);
 }

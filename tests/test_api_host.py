@@ -72,10 +72,12 @@ def test_workspace_and_partition_sizes():
     assert pa.partition_size(4, 64, 8, 128, 131072, 512) == 512
     assert pa.partition_size(4, 64, 8, 128, 131072, 0) % 16 == 0
     assert pa.partition_size(4, 64, 8, 128, 131072, 24) == 0
-    # 4 x 64 heads x 256 partitions x (8 B of (m, l) + 128 x 4 B of o)
+    # 256-byte header, then 4 x 64 heads x 256 partitions x (8 B of (m, l)),
+    # then the o records (128 x 4 B each), 256-byte aligned
     n = 4 * 64 * 256
-    assert pa.workspace_size(4, 64, 8, 128, 131072, 512) == n * 8 + n * 512
-    assert pa.workspace_size(4, 64, 8, 128, 100, 512) == 4 * 64 * (8 + 512) + (256 - 4 * 64 * 8 % 256) % 256
+    assert pa.workspace_size(4, 64, 8, 128, 131072, 512) == 256 + n * 8 + n * 512
+    n = 4 * 64
+    assert pa.workspace_size(4, 64, 8, 128, 100, 512) == 256 + 2048 + n * 512
 
 
 def test_write_validation():

@@ -65,7 +65,8 @@ def test_poison_covers_unused_and_tails(name):
         assert np.all(np.isnan(v["k_pool"][bad])) and np.all(np.isnan(v["v_pool"][bad]))
         assert not np.isnan(v["k_pool"][~bad]).any()
     else:
-        assert np.all(np.isnan(v["k_scale"][bad])) and not np.isnan(v["k_scale"][~bad]).any()
+        ks = v["k_scale"].transpose(0, 2, 1)
+        assert np.all(np.isnan(ks[bad])) and not np.isnan(ks[~bad]).any()
     # determinism
     v2 = gen.fill_numpy(gen.make(name, small=True), new_slot_poison=False)
     assert np.array_equal(v["q"], v2["q"])

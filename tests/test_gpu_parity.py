@@ -117,7 +117,7 @@ def test_write_kv_int8_matches_oracle_quantiser(pa):
     slots = rng.permutation(NB * 16)[:T].astype(np.int32)
     slots[7] = -1
     kp = np.zeros((NB, 16, Hkv, D), np.int8)
-    ks = np.full((NB, 16, Hkv), -1.0, np.float32)
+    ks = np.full((NB, Hkv, 16), -1.0, np.float32)
     dk, dv, dks, dvs = t(kp), t(kp), t(ks), t(ks)
     pa.write_kv_int8(t(x[0]), t(x[1]), t(slots), dk, dv, dks, dvs)
     for which, src, dp, ds in ((0, x[0], dk, dks), (1, x[1], dv, dvs)):
@@ -126,7 +126,7 @@ def test_write_kv_int8_matches_oracle_quantiser(pa):
         for i, s in enumerate(slots):
             if s >= 0:
                 want_p[s // 16, s % 16] = codes[i]
-                want_s[s // 16, s % 16] = sc[i]
+                want_s[s // 16, :, s % 16] = sc[i]
         assert np.array_equal(dp.cpu().numpy(), want_p), which
         assert np.array_equal(ds.cpu().numpy().view(np.uint32), want_s.view(np.uint32)), which
 
@@ -271,15 +271,21 @@ def test_partials_plus_merge_equals_decode(pa):
                            v_scale=d["v_scale"])
     b = pa.merge_partials(ws, d["context_lens"], wl.q_heads, wl.head_dim, P, wl.max_context_len)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    # records against the oracle's own partition statistics (log2 units)
+    # records against the oracle's own partition statistics (log2 units);
+    # workspace: 256-byte header (int32 partitions per record), then (m, l)
     n_part = -(-wl.max_context_len // P)
-    ml = ws[:wl.batch * wl.q_heads * n_part * 8].view(torch.float32).view(
+    span = int(ws[:4].view(torch.int32).item())
+    assert span == 1          # a two-sequence batch keeps one partition per record
+    ml = ws[256:256 + wl.batch * wl.q_heads * n_part * 8].view(torch.float32).view(
         wl.batch, wl.q_heads, n_part, 2).cpu().numpy()
     parts = ref.ref_partials(vals["q"], vals["k_pool"], vals["v_pool"], wl.block_table,
                              wl.context_lens, wl.scale, P, vals["k_scale"], vals["v_scale"])
+    # (m, l) is a reference point and the sum of 2^(s - m) over the
+    # partition: m + log2(l) is the partition's log-sum-exp (log2 units)
     m, l, _ = parts[1][5]
-    np.testing.assert_allclose(ml[1, 5, :len(m), 0] * math.log(2), m, rtol=0, atol=1e-4)
-    np.testing.assert_allclose(ml[1, 5, :len(m), 1], l, rtol=1e-4)
+    lse_gpu = (ml[1, 5, :len(m), 0] + np.log2(ml[1, 5, :len(m), 1])) * math.log(2)
+    np.testing.assert_allclose(lse_gpu, m + np.log(l), rtol=0, atol=1e-4)
+    assert np.all(ml[1, 5, :len(m), 0] * math.log(2) <= m + 1e-4)
 
 
 def test_bad_metadata_gives_nan_rows_not_faults(pa):
@@ -343,3 +349,24 @@ def test_full_size_sampled_rows(pa, name):
     want, _ = oracle_decode(wl, host, rows=rows)
     got = np.stack([out[b, h] for b, h in rows])
     check_close(got, np.stack([want[b, h] for b, h in rows]), f"{name} sampled rows")
+
+
+def test_runs_of_partitions_merged_online(pa):
+    """A long context in a small batch: the matrix-core kernel merges runs of
+    consecutive partitions online (span > 1, read back from the workspace
+    header) and the merge kernel combines the run records."""
+    over = dict(batch=1, q_heads=8, kv_heads=1, head_dim=64, ctx=70000, scatter=0.15,
+                kv_dtype="fp16", partition_size=16)
+    wl = gen.make("long128k_int8", seed=91, overrides=over)
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    d = device_inputs(wl, vals)
+    need = pa.workspace_size(1, 8, 1, 64, wl.max_context_len, 16)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    out = pa.decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"],
+                    scale=wl.scale, partition_size=16, max_context_len=wl.max_context_len,
+                    workspace=ws)
+    span = int(ws[:4].view(torch.int32).item())
+    say(f"runs: L={wl.max_context_len} P=16 span={span}")
+    assert span == 2            # 4375 partitions -> 2188 runs >= 2048 waves
+    want, _ = oracle_decode(wl, vals)
+    check_close(out.cpu().numpy(), want, "span-2 runs")

@@ -30,8 +30,8 @@ def tiny_case(rng, B, Hq, Hkv, D, lens, nb=None, int8=False):
     if int8:
         k = rng.integers(-127, 128, (nb, 16, Hkv, D), dtype=np.int8)
         v = rng.integers(-127, 128, (nb, 16, Hkv, D), dtype=np.int8)
-        ks = rng.uniform(0.01, 0.03, (nb, 16, Hkv)).astype(np.float32)
-        vs = rng.uniform(0.01, 0.03, (nb, 16, Hkv)).astype(np.float32)
+        ks = rng.uniform(0.01, 0.03, (nb, Hkv, 16)).astype(np.float32)
+        vs = rng.uniform(0.01, 0.03, (nb, Hkv, 16)).astype(np.float32)
     else:
         k = rng.standard_normal((nb, 16, Hkv, D), dtype=np.float32).astype(np.float16)
         v = rng.standard_normal((nb, 16, Hkv, D), dtype=np.float32).astype(np.float16)

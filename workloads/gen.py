@@ -2,7 +2,7 @@
 
 This module only *draws inputs*: context lengths, block tables, new-token
 slots, and Q / K / V values (fp16, or int8 codes plus fp32 per-(token, kv-head)
-scales).  It computes none of the attention, quantisation or KV-write
+scales, laid out [num_blocks, kv_heads, 16]).  It computes none of the attention, quantisation or KV-write
 arithmetic, so the CPU oracle side and the GPU side of a test can both take
 their inputs from here without sharing any of the method.
 
@@ -265,8 +265,8 @@ def fill_numpy(wl: Workload, *, new_slot_poison: bool = True) -> dict[str, np.nd
     else:
         v["k_pool"] = rng.integers(-127, 128, size=(NB, BLOCK, Hkv, D), dtype=np.int8)
         v["v_pool"] = rng.integers(-127, 128, size=(NB, BLOCK, Hkv, D), dtype=np.int8)
-        v["k_scale"] = rng.uniform(2.3 / 127, 3.8 / 127, size=(NB, BLOCK, Hkv)).astype(np.float32)
-        v["v_scale"] = rng.uniform(2.3 / 127, 3.8 / 127, size=(NB, BLOCK, Hkv)).astype(np.float32)
+        v["k_scale"] = rng.uniform(2.3 / 127, 3.8 / 127, size=(NB, Hkv, BLOCK)).astype(np.float32)
+        v["v_scale"] = rng.uniform(2.3 / 127, 3.8 / 127, size=(NB, Hkv, BLOCK)).astype(np.float32)
     v["k_new"] = _normal16(rng, (B, Hkv, D))
     v["v_new"] = _normal16(rng, (B, Hkv, D))
     if wl.poison:
@@ -280,8 +280,8 @@ def fill_numpy(wl: Workload, *, new_slot_poison: bool = True) -> dict[str, np.nd
             v["k_pool"][bad] = nan16
             v["v_pool"][bad] = nan16
         else:
-            v["k_scale"][bad] = np.nan
-            v["v_scale"][bad] = np.nan
+            v["k_scale"].transpose(0, 2, 1)[bad] = np.nan    # scales are [NB, Hkv, 16]
+            v["v_scale"].transpose(0, 2, 1)[bad] = np.nan
     wl.values = v
     return v
 
@@ -315,7 +315,7 @@ def fill_torch(wl: Workload, device, *, chunk_rows: int = 1 << 12) -> dict[str, 
             v[nm] = torch.randint(-127, 128, (NB, BLOCK, Hkv, D), generator=gen,
                                   device=dev, dtype=torch.int8)
         for nm in ("k_scale", "v_scale"):
-            t = torch.rand((NB, BLOCK, Hkv), generator=gen, device=dev, dtype=torch.float32)
+            t = torch.rand((NB, Hkv, BLOCK), generator=gen, device=dev, dtype=torch.float32)
             v[nm] = t * (1.5 / 127) + (2.3 / 127)
     v["k_new"] = normal16((B, Hkv, D))
     v["v_new"] = normal16((B, Hkv, D))
@@ -325,8 +325,8 @@ def fill_torch(wl: Workload, device, *, chunk_rows: int = 1 << 12) -> dict[str, 
             v["k_pool"][bad] = float("nan")
             v["v_pool"][bad] = float("nan")
         else:
-            v["k_scale"][bad] = float("nan")
-            v["v_scale"][bad] = float("nan")
+            v["k_scale"].permute(0, 2, 1)[bad] = float("nan")
+            v["v_scale"].permute(0, 2, 1)[bad] = float("nan")
     wl.values = v
     return v
 
