@@ -40,7 +40,6 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "paged-attn decode: achieved KV HBM GB/s (% of peak) and sequences/s per layer"
 HEADLINE = "llama2_7b"
 OTHERS = ["gqa70b_mixed", "prefix_shared", "long128k_int8", "tiny_gqa"]
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_238_amd", "csrc", "decode.hip")
 
 
 def parse():
@@ -59,15 +58,31 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the "
                          "known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--counters-summary", nargs=5, default=None,
+                    metavar=("OUT_JSON", "DECODE_FETCH_DIR", "DECODE_WRITE_DIR",
+                             "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="host only: summarise rocprofv3 --pmc databases of a decode "
+                         "run (FETCH_SIZE, WRITE_SIZE) and of a --copy-calibration run "
+                         "into OUT_JSON (uses --workload and --copy-calibration MIB)")
     return ap.parse_args()
 
 
+KERNEL_SOURCES = ("decode.hip", "decode_mfma.hip", "merge.hip", "run_span.h", "pa_internal.h",
+                  "pa_api.hip", "write_kv.hip")
+
+
 def source_hash() -> str:
+    """Hash of the kernel sources; counter summaries carry the hash they were
+    taken on and are ignored once it changes."""
     h = hashlib.sha256()
-    for name in ("decode.hip", "merge.hip", "pa_internal.h"):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "paged_kv_cache_238_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def decode_kernel_name(wl) -> str:
+    return "decode_valu_kernel" if wl.q_heads // wl.kv_heads <= 2 else "decode_mfma_kernel"
 
 
 class Case:
@@ -175,7 +190,7 @@ def summarize(case, wall, kern_ms, steps):
 def traffic_for(name):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"decode_partition_{name}_counters.json")
+    path = os.path.join(ROOT, "profiles", f"decode_{name}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -183,6 +198,64 @@ def traffic_for(name):
     if c.get("source_hash") != source_hash():
         return None
     return c.get("traffic_bytes_per_launch")
+
+
+def _counter_means(directory, counter):
+    """kernel name -> (dispatches, mean value per dispatch) from a rocpd db."""
+    import glob
+    import sqlite3
+    out = {}
+    for db in glob.glob(os.path.join(directory, "**", "*.db"), recursive=True):
+        con = sqlite3.connect(db)
+        rows = con.execute("select kernel_name, value from counters_collection "
+                           "where counter_name = ?", (counter,)).fetchall()
+        acc = {}
+        for name, val in rows:
+            acc.setdefault(name, []).append(val)
+        for name, vals in acc.items():
+            out[name] = (len(vals), sum(vals) / len(vals))
+    return out
+
+
+def counters_summary(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode kernel,
+    scaled by what the same counters read for a plain copy of known size."""
+    from workloads import gen
+    out_json, dfetch, dwrite, cfetch, cwrite = args.counters_summary
+    wl = gen.make(args.workload, poison=False)
+    kname = decode_kernel_name(wl)
+    known = args.copy_calibration << 20
+
+    def pick(table, key):
+        hits = {k: v for k, v in table.items() if key in k}
+        if not hits:
+            raise SystemExit(f"no dispatch of a kernel named like {key!r}")
+        return max(hits.items(), key=lambda kv: kv[1][1])
+
+    def copy_kernel(table):     # the copy: the dispatch with the largest counter
+        return max(table.items(), key=lambda kv: kv[1][1])
+
+    cf_name, (cf_n, cf) = copy_kernel(_counter_means(cfetch, "FETCH_SIZE"))
+    cw_name, (cw_n, cw) = copy_kernel(_counter_means(cwrite, "WRITE_SIZE"))
+    df_name, (df_n, df) = pick(_counter_means(dfetch, "FETCH_SIZE"), kname)
+    dw_name, (dw_n, dw) = pick(_counter_means(dwrite, "WRITE_SIZE"), kname)
+    f_fetch = known / (cf * 1024.0)
+    f_write = known / (cw * 1024.0)
+    traffic = df * 1024.0 * f_fetch + dw * 1024.0 * f_write
+    res = {
+        "workload": wl.name, "kernel": df_name, "source_hash": source_hash(),
+        "decode_fetch_kib_per_dispatch": df, "decode_write_kib_per_dispatch": dw,
+        "decode_dispatches": [df_n, dw_n],
+        "copy_kernel": cf_name, "copy_bytes": known,
+        "copy_fetch_kib_per_dispatch": cf, "copy_write_kib_per_dispatch": cw,
+        "fetch_scale": f_fetch, "write_scale": f_write,
+        "traffic_bytes_per_launch": round(traffic),
+        "algorithmic_bytes_per_launch": gen.kv_ideal_bytes(wl),
+        "traffic_over_algorithmic": round(traffic / gen.kv_ideal_bytes(wl), 4),
+    }
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=2)
+    print(json.dumps(res, indent=2))
 
 
 def cpu_baseline(case, budget_s):
@@ -218,6 +291,9 @@ def cpu_baseline(case, budget_s):
 
 def main():
     args = parse()
+    if args.counters_summary:
+        counters_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path runs on a single device)", file=sys.stderr)
@@ -277,7 +353,7 @@ def main():
         "config": {k: s[k] for k in ("workload", "batch", "q_heads", "kv_heads", "head_dim",
                                      "block_size", "kv_dtype", "max_context_len",
                                      "partition_size", "n_part", "kv_bytes")},
-        "roofline": {"bound": "hbm", "kernel": "decode_valu_kernel (partition)",
+        "roofline": {"bound": "hbm", "kernel": decode_kernel_name(head.wl),
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes_per_launch": s["kv_bytes"],
