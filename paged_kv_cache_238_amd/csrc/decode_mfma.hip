@@ -41,17 +41,29 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;   // at most four waves (kv heads) per workgroup
+constexpr int kThreads = 512;   // at most eight waves (kv heads) per workgroup
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.693147180559945309f;
 #ifndef PA_V_ROW_PAD
 #define PA_V_ROW_PAD 16
 #endif
 constexpr int kRowPad = PA_V_ROW_PAD;   // bytes of padding per LDS row of the V tile
+// Register sets the block loads rotate through (NBUF - 1 blocks in flight
+// while one is reduced).
+#ifndef PA_MFMA_NBUF_I8
+#define PA_MFMA_NBUF_I8 3
+#endif
+#ifndef PA_MFMA_NBUF_F16
+#define PA_MFMA_NBUF_F16 2
+#endif
+#ifndef PA_MFMA_WAVES_PER_EU
+#define PA_MFMA_WAVES_PER_EU 3
+#endif
 // The running max is only moved (and the accumulators rescaled) when a block
 // beats it by more than this many log2 units; softmax is invariant to the
 // reference point, and probabilities stay <= 2^8, well inside fp16.
 constexpr float kRescaleSlack = 8.0f;
+constexpr int kLongContext = 32768;   // tokens; see waves_per_group
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -122,16 +134,17 @@ struct Geometry {
   static constexpr int kRowBytes = D * 2 + kRowPad;   // LDS row of the fp16 V tile
 };
 
-// Three waves per SIMD (<= 168 registers): memory-level parallelism is what
-// bounds this kernel, so occupancy is worth more than deeper unrolling.
+// Three waves per SIMD (<= 168 registers) with two (fp16) or three (int8)
+// register sets of block loads; deeper rotation at two waves per SIMD and
+// four waves per SIMD with fewer sets both measured slower.
 //
-// Work split: a workgroup holds `wpg` waves (1, 2 or 4) for wpg consecutive
+// Work split: a workgroup holds `wpg` waves (1, 2, 4 or 8) for wpg consecutive
 // kv heads of one (sequence, partition); each wave streams its own head's
 // whole partition and writes its own record.  The waves of a workgroup thus
 // read neighbouring slices of the same token rows at the same time, and a
 // wave's start-up (length, block ids, Q) is paid once per partition.
 template <int D, int G, bool I8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES_PER_EU)))
 void decode_mfma_kernel(const DecodeParams p) {
   using Geo = Geometry<D, I8>;
   constexpr int NLD = Geo::kLoads;
@@ -443,33 +456,19 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
   };
   if (nfull > 0) {
-    if constexpr (I8) {
-      Regs A, B, C;
-      issue(0, A);
-      issue(1, B);
-      for (int k = 0; k < nfull; k += 3) {
-        issue(k + 2, C);
+    constexpr int NBUF = I8 ? PA_MFMA_NBUF_I8 : PA_MFMA_NBUF_F16;
+    Regs R[NBUF];
+#pragma unroll
+    for (int s = 0; s + 1 < NBUF; ++s) issue(s, R[s]);
+    for (int k = 0; k < nfull; k += NBUF) {
+#pragma unroll
+      for (int s = 0; s < NBUF; ++s) {
+        issue(k + s + NBUF - 1, R[(s + NBUF - 1) % NBUF]);
         __builtin_amdgcn_sched_barrier(0);
-        process_block(full, A, kBlockTokens);
-        done(k);
-        issue(k + 3, A);
-        __builtin_amdgcn_sched_barrier(0);
-        if (k + 1 < nfull) { process_block(full, B, kBlockTokens); done(k + 1); }
-        issue(k + 4, B);
-        __builtin_amdgcn_sched_barrier(0);
-        if (k + 2 < nfull) { process_block(full, C, kBlockTokens); done(k + 2); }
-      }
-    } else {
-      Regs A, B;
-      issue(0, A);
-      for (int k = 0; k < nfull; k += 2) {
-        issue(k + 1, B);
-        __builtin_amdgcn_sched_barrier(0);
-        process_block(full, A, kBlockTokens);
-        done(k);
-        issue(k + 2, A);
-        __builtin_amdgcn_sched_barrier(0);
-        if (k + 1 < nfull) { process_block(full, B, kBlockTokens); done(k + 1); }
+        if (s == 0 || k + s < nfull) {
+          process_block(full, R[s], kBlockTokens);
+          done(k + s);
+        }
       }
     }
   }
@@ -482,10 +481,19 @@ void decode_mfma_kernel(const DecodeParams p) {
   finalize();
 }
 
+// Waves (kv heads) per workgroup.  Long contexts (runs of many blocks, all
+// alike): eight, so one workgroup reads whole token rows of an 8-head cache.
+// Otherwise four, which keeps workgroups small enough to pack CUs evenly
+// when runs are short or uneven.
+int waves_per_group(const DecodeParams& p) {
+  if (p.kv_heads % 8 == 0 && p.max_context_len >= kLongContext) return 8;
+  return (p.kv_heads % 4 == 0) ? 4 : (p.kv_heads % 2 == 0) ? 2 : 1;
+}
+
 template <int D, int G, bool I8>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   using Geo = Geometry<D, I8>;
-  const int wpg = (p.kv_heads % 4 == 0) ? 4 : (p.kv_heads % 2 == 0) ? 2 : 1;
+  const int wpg = waves_per_group(p);
   const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes;
   // runs never outnumber partitions, so n_part bounds the run index
   const unsigned grid = (unsigned)p.n_part * p.batch * (p.kv_heads / wpg);

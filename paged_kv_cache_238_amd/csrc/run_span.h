@@ -23,16 +23,18 @@ __device__ inline int run_span(const int32_t* context_lens, int batch, int kv_he
   if ((long long)batch * kv_heads >= target_waves) return 1;
   const int lane = threadIdx.x & 63;
   const int max_part = (max_context_len + partition_size - 1) / partition_size;
+  auto parts = [&](int b) {                  // partitions of sequence b (0 if invalid)
+    if (b >= batch) return 0;
+    const int L = context_lens[b];
+    return (L > 0 && L <= max_context_len) ? (L + partition_size - 1) / partition_size : 0;
+  };
+  const int n0 = parts(lane);                // batches of up to 64 need one load
   int span = 1;
   for (int s = 2; s <= max_part; s *= 2) {
     long long runs = 0;
     for (int b0 = 0; b0 < batch; b0 += 64) {
-      int r = 0;
-      if (b0 + lane < batch) {
-        const int L = context_lens[b0 + lane];
-        const int n = (L > 0 && L <= max_context_len) ? (L + partition_size - 1) / partition_size : 0;
-        r = (n + s - 1) / s;
-      }
+      const int n = b0 == 0 ? n0 : parts(b0 + lane);
+      int r = (n + s - 1) / s;
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) r += __shfl_xor(r, off);
       runs += r;

@@ -370,3 +370,20 @@ def test_runs_of_partitions_merged_online(pa):
     assert span == 2            # 4375 partitions -> 2188 runs >= 2048 waves
     want, _ = oracle_decode(wl, vals)
     check_close(out.cpu().numpy(), want, "span-2 runs")
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_long_context_eight_head_workgroups(pa, int8):
+    """Contexts of 32K+ tokens with 8 kv heads run eight-wave workgroups
+    (one per kv head of a token row); a shorter sequence in the same batch
+    and a ragged tail ride along."""
+    over = dict(batch=2, q_heads=64, kv_heads=8, head_dim=64, ctx=33003, scatter=0.15,
+                kv_dtype="int8" if int8 else "fp16", partition_size=512)
+    wl = gen.make("long128k_int8", seed=93 + int8, overrides=over)
+    wl.context_lens[1] = 20000
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    d = device_inputs(wl, vals)
+    say(f"long ctx 8-wave groups int8={int8} lens={wl.context_lens.tolist()}")
+    out = gpu_decode(pa, wl, d, partition_size=512, return_lse=False)
+    want, _ = oracle_decode(wl, vals)
+    check_close(out.cpu().numpy(), want, f"long ctx int8={int8}")
