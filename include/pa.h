@@ -117,7 +117,11 @@ int pa_write_kv_int8(const void* k_new, const void* v_new, const int32_t* slot_m
 
 /*
  * Partition size the library uses for these shapes when partition_size is
- * 0, else partition_size itself (a multiple of 16).  Returns 0 on invalid
+ * 0, else partition_size itself (a multiple of 16).  The library's choice:
+ * 256 tokens, the finest split, with runs of partitions merged on the
+ * device (see the workspace layout below); or, when batch * kv_heads alone
+ * reaches 2048 (enough waves to fill the GPU), one partition covering
+ * max_context_len rounded up to 16, so no merge runs.  Returns 0 on invalid
  * arguments.
  */
 int pa_decode_partition_size(int batch, int q_heads, int kv_heads, int head_dim,
@@ -186,11 +190,13 @@ int pa_decode_int8(void* out, float* lse_out, const void* q, const int8_t* k_poo
  *   int32  header[64]                   header[0] = span: partitions per
  *                                       record.  Record r of (b, h) covers
  *                                       partitions [r*span, (r+1)*span).
- *                                       span is 1 for groups of 1 or 2; for
- *                                       larger groups it is chosen on the
- *                                       device from the context lengths
- *                                       (long contexts: several partitions
- *                                       merged online by one wave).
+ *                                       span is chosen on the device from
+ *                                       the context lengths: the largest
+ *                                       power of two that leaves at least
+ *                                       2048 (record, kv head) runs over
+ *                                       the batch (1 when batch * kv_heads
+ *                                       alone reaches 2048); one wave
+ *                                       merges a run's partitions online.
  *   float2 ml[batch][q_heads][n_part]   (m, l): m = a reference point in
  *                                       log2 units, at most the partition's
  *                                       largest score s = scale * log2(e) *

@@ -2,12 +2,12 @@
 // used for query-head groups of 1 or 2 (larger groups use the matrix-core
 // kernel in decode_mfma.hip).
 //
-// One workgroup = one (partition, kv head, sequence).  Its four wave64s walk
-// the partition's 16-token blocks (wave w takes blocks w, w+4, ...), each
-// keeping an online-softmax state for every query head of the kv head's
-// group, then merge their states through LDS.  The result is either the
-// final fp16 row (whole context in one partition) or one partition record
-// (max, sum, unnormalised output) for the log-sum-exp merge kernel.
+// Work split (as in the matrix-core kernel): a workgroup holds up to four
+// waves for consecutive kv heads of one (sequence, run); each wave streams
+// its head's run of partitions - sized on the device from the actual
+// context lengths (run_span.h) - merges it online and writes one record
+// (max reference, sum, unnormalised output) for the log-sum-exp merge
+// kernel, or the final fp16 row when one partition covers the context.
 //
 // Method: the zskr.cn article on ATB's PagedAttention, section
 // "PagedAttention 的 Attention 计算修改" - per-page gather through the page
@@ -16,19 +16,19 @@
 // listing: the running max is updated before the new term's exponent is
 // taken, the max starts at -inf, a softmax scale is applied, accumulation is
 // fp32, the output is indexed by head, and tail slots are masked.  The page
-// table slice is staged in LDS once per workgroup (section "踩坑一").
-// Query heads h = g*G .. g*G+G-1 share kv head g (discosf.com article
-// "KV Cache 优化与显存管理", section "二、优化方向").
+// table slice is read once per wave and held one id per lane (section
+// "踩坑一").  Query heads h = g*G .. g*G+G-1 share kv head g (discosf.com
+// article "KV Cache 优化与显存管理", section "二、优化方向").
 //
 // Lane layout: a K/V row (one token, one kv head) of D elements is split
 // over D/8 lanes holding 8 consecutive elements each (16 B for fp16, 8 B for
 // int8), so one wave-wide load covers 64/(D/8) token rows.  Lanes holding
 // the same token ("row group") reduce their partial dot products with DPP;
 // every row group keeps its own running (max, sum, acc) so the hot loop has
-// no cross-row traffic; row groups and waves are merged once at the end.
-// Scores are kept in log2 units (scale * log2 e folded in), so exp is one
-// v_exp_f32.
+// no cross-row traffic; row groups are merged once per run.  Scores are
+// kept in log2 units (scale * log2 e folded in), so exp is one v_exp_f32.
 #include "pa_internal.h"
+#include "run_span.h"
 
 #include <type_traits>
 
@@ -118,67 +118,75 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   constexpr int NL = kBlockTokens / RPW;     // wave loads per block
   using Chunk = typename KvChunk<I8>::T;
   constexpr int ESZ = I8 ? 1 : 2;
-  extern __shared__ float smem[];
 
-  // 1-D grid, partition slowest (see the matrix-core kernel): consecutive
-  // workgroups, which land on different XCDs, are different (sequence, kv
-  // head) pairs of one partition index.
-  const int pairs = p.batch * p.kv_heads;
-  const int part = blockIdx.x / pairs;
-  const int b = (blockIdx.x % pairs) / p.kv_heads, g = (blockIdx.x % pairs) % p.kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wpg = blockDim.x >> 6;           // kv heads per workgroup
   const int r = lane / LPR, c = lane % LPR;
   const int Hq = p.q_heads, Hkv = p.kv_heads;
+
+  // 1-D grid, run index slowest: consecutive workgroups (dealt round-robin
+  // to the eight XCDs) are the head groups and sequences of one run index.
+  const int groups = Hkv / wpg;
+  const int per_run = p.batch * groups;
+  const int ridx = blockIdx.x / per_run;
+  const int rem = blockIdx.x % per_run;
+  const int b = rem / groups;
+  const int g = (rem % groups) * wpg + w;
   const int h0 = g * G;
 
-  if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = 1;   // one partition per record
-  const int L = p.context_lens[b];
   const int P = p.partition_size;
-  const int t_begin = part * P;
-  if (L < 0 || L > p.max_context_len) {
-    // broken metadata: NaN rows, written once
-    if (part == 0) {
-      for (int i = tid; i < G * D; i += kThreads) {
-        const int h = h0 + i / D, d = i % D;
-        const size_t row = (size_t)b * Hq + h;
-        if (p.direct) {
-          p.out[row * D + d] = 0x7E00;
-          if (d == 0 && p.lse) p.lse[row] = __builtin_nanf("");
-        }
-      }
-    }
-    return;
-  }
-  if (t_begin >= L) {
-    if (p.direct && part == 0) {   // L == 0: zero row, lse = -inf
-      for (int i = tid; i < G * D; i += kThreads) {
-        const int h = h0 + i / D, d = i % D;
-        const size_t row = (size_t)b * Hq + h;
-        p.out[row * D + d] = 0;
-        if (d == 0 && p.lse) p.lse[row] = kNegInf;
-      }
-    }
-    return;
-  }
-  const int t_end = min(t_begin + P, L);
-  const int ntok = t_end - t_begin;
-  const int nblk = (ntok + kBlockTokens - 1) / kBlockTokens;
-  const int j0 = t_begin / kBlockTokens;
+  const int span = p.direct ? 1 : run_span(p.context_lens, p.batch, Hkv, p.max_context_len, P,
+                                           p.target_waves);
+  if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = span;
+  const int t_begin = ridx * span * P;
+  const int j0 = min(t_begin / kBlockTokens, p.max_blocks - 1);
+  const int32_t* bt_row = p.block_table + (size_t)b * p.max_blocks;
 
-  // Stage this partition's slice of the block table in LDS, once.
-  int* s_ids = reinterpret_cast<int*>(smem);
-  {
-    const int32_t* row = p.block_table + (size_t)b * p.max_blocks + j0;
-    for (int i = tid; i < nblk; i += kThreads) s_ids[i] = row[i];
-  }
-  __syncthreads();
-
+  // Start-up loads, all independent: length, first 64 block ids of the run
+  // (clamped to the table row), Q.
+  const int L = p.context_lens[b];
+  const int row_left = p.max_blocks - j0;
+  const int span_blocks = span * (P / kBlockTokens);
+  // Block ids c0 .. c0+63 of the run, one per lane, through a buffer
+  // resource bounded to the run's slice of the table row: ids past the
+  // slice read as 0 with no branch, so the load stays asynchronous.
+  const __amdgpu_buffer_rsrc_t rids =
+      make_rsrc(bt_row + j0, (uint32_t)max(min(span_blocks, row_left), 0) * 4u);
+  auto load_ids = [&](int c0) {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(rids, (uint32_t)(c0 + lane) * 4u, 0, 0);
+  };
+  int ids = load_ids(0);
   // Query slice of every head in the group: elements c*8 .. c*8+7.
   uint4 qraw[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
     qraw[hh] = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * Hq + h0 + hh) * D + c * 8);
+
+  if (L < 0 || L > p.max_context_len) {      // broken metadata: NaN rows
+    if (ridx == 0 && p.direct) {
+      for (int i = lane; i < G * D; i += 64) {
+        const size_t row = (size_t)b * Hq + h0 + i / D;
+        p.out[row * D + i % D] = 0x7E00;
+        if (i % D == 0 && p.lse) p.lse[row] = __builtin_nanf("");
+      }
+    }
+    return;
+  }
+  if (t_begin >= L) {                        // empty run (L == 0: zero row)
+    if (p.direct && ridx == 0) {
+      for (int i = lane; i < G * D; i += 64) {
+        const size_t row = (size_t)b * Hq + h0 + i / D;
+        p.out[row * D + i % D] = 0;
+        if (i % D == 0 && p.lse) p.lse[row] = kNegInf;
+      }
+    }
+    return;
+  }
+  const int ntok = min(t_begin + span_blocks * kBlockTokens, L) - t_begin;
+  const int nfull = ntok / kBlockTokens;
+  const int tail = ntok - nfull * kBlockTokens;
+
   float qf[I8 ? G : 1][8];
   if constexpr (I8) {
 #pragma unroll
@@ -207,6 +215,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   for (int i = 0; i < NL; ++i) scale_off[i] = (uint32_t)g * kBlockTokens + r + RPW * i;   // [NB, Hkv, 16]
   const char* kbase = static_cast<const char*>(p.k_pool);
   const char* vbase = static_cast<const char*>(p.v_pool);
+  const uint32_t scale_blk_bytes = (uint32_t)kBlockTokens * Hkv * sizeof(float);
 
   struct Regs {
     Chunk k[NL];
@@ -215,14 +224,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     float vs[NL];
   };
 
-  // Issue every K load of block jj, then every V load (V arrives while the
-  // scores are computed).  real == false: a prefetch past the last block;
-  // its loads are out of range of an empty resource and fetch nothing.
-  const uint32_t scale_blk_bytes = (uint32_t)kBlockTokens * Hkv * sizeof(float);
-  auto load_block = [&](int jj, bool real, Regs& R) {
-    int blk = __builtin_amdgcn_readfirstlane(s_ids[real ? jj : 0]);
+  // Every K load of a block, then every V load (V arrives while the scores
+  // are computed).  real == false: a prefetch past the end; its resource is
+  // empty, so the loads return zeros without touching memory.
+  auto load_block = [&](int blk, bool real, Regs& R) {
     if ((unsigned)blk >= (unsigned)p.num_blocks) {
-      if (real) bad_blk = true;   // the result becomes NaN; read nothing
+      if (real) bad_blk = true;              // the record becomes NaN
       real = false;
       blk = 0;
     }
@@ -235,8 +242,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     for (int i = 0; i < NL; ++i) buffer_load(R.v[i], rv, lane_off[i]);
     if constexpr (I8) {
       const uint32_t sbytes = real ? scale_blk_bytes : 0u;
-      const __amdgpu_buffer_rsrc_t rks = make_rsrc(p.k_scale + (size_t)blk * kBlockTokens * Hkv, sbytes);
-      const __amdgpu_buffer_rsrc_t rvs = make_rsrc(p.v_scale + (size_t)blk * kBlockTokens * Hkv, sbytes);
+      const size_t sblk = (size_t)blk * kBlockTokens * Hkv;
+      const __amdgpu_buffer_rsrc_t rks = make_rsrc(p.k_scale + sblk, sbytes);
+      const __amdgpu_buffer_rsrc_t rvs = make_rsrc(p.v_scale + sblk, sbytes);
 #pragma unroll
       for (int i = 0; i < NL; ++i) R.ks[i] = buffer_load_f32(rks, scale_off[i] * 4u);
 #pragma unroll
@@ -320,113 +328,113 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     }
   };
 
-  // Full blocks of this wave: w, w+4, ...  Two register sets alternate so
-  // the loads of the next block are in flight while the current one is
-  // reduced.  Loads sit outside every branch (prefetches past the end read
-  // nothing) and all branches are wave-uniform, so the waits stay exact.
-  const int nfull = ntok / kBlockTokens;
-  const int nmine = nfull > w ? (nfull - w + kWaves - 1) / kWaves : 0;
-  if (nmine > 0) {
-    std::integral_constant<bool, false> full;
-    Regs A, B;
-    load_block(w, true, A);
-    for (int k = 0; k < nmine; k += 2) {
-      load_block(w + (k + 1) * kWaves, k + 1 < nmine, B);
-      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the math
-      process_block(full, A, kBlockTokens);
-      load_block(w + (k + 2) * kWaves, k + 2 < nmine, A);
+  // Record of the run: merge the RPW row groups, then store.
+  auto finalize = [&]() {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float M = m[hh];
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+      const float f = fast_exp2(m[hh] - ((M == kNegInf) ? 0.f : M));
+      float den = l[hh] * f;
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) den += __shfl_xor(den, off);
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = acc[hh][e] * f;
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
+        o[e] = x;
+      }
+      if (bad_blk) M = den = __builtin_nanf("");
+      if (r == 0) {                          // lanes c = 0 .. LPR-1 hold dims c*8 .. c*8+7
+        const size_t row = (size_t)b * Hq + h0 + hh;
+        if (p.direct) {
+          const float inv = 1.0f / den;
+          uint4 pk;
+          uint32_t* pw = reinterpret_cast<uint32_t*>(&pk);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pw[e] = (uint32_t)f32_to_f16_bits(o[2 * e] * inv) |
+                    ((uint32_t)f32_to_f16_bits(o[2 * e + 1] * inv) << 16);
+          if (bad_blk) pk = make_uint4(0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u);
+          *reinterpret_cast<uint4*>(p.out + row * D + c * 8) = pk;
+          if (c == 0 && p.lse) p.lse[row] = (M + log2f(den)) * kLn2;
+        } else {
+          const size_t rec = row * p.n_part + ridx;
+          float4* dst = reinterpret_cast<float4*>(p.part_o + rec * D + c * 8);
+          float4 a = make_float4(o[0], o[1], o[2], o[3]);
+          float4 bq = make_float4(o[4], o[5], o[6], o[7]);
+          if (bad_blk) a = bq = make_float4(M, M, M, M);
+          dst[0] = a;
+          dst[1] = bq;
+          if (c == 0) p.part_ml[rec] = make_float2(M, den);
+        }
+      }
+    }
+  };
+
+  // Blocks of the run, streamed in order.  Block ids come one per lane from
+  // `ids`, a 64-block chunk; the following chunk is fetched into `ids_next`
+  // a whole chunk ahead and moved over just before its first block is
+  // issued, so no issue reads a register whose load may still be pending.
+  // Two register sets alternate, so one block is in flight while the other
+  // is reduced; block j always lands in R[j % 2].  The partial last block
+  // (only in a sequence's last run) is fetched through the same pipeline as
+  // block nfull and reduced after the loop; later prefetches read nothing
+  // (empty resource) and, with two sets, never land on the tail's set.
+  // Every branch is wave-uniform and no load sits inside one, so the waits
+  // stay exact.
+  constexpr int NBUF = 2;
+  const int nreal = nfull + (tail > 0 ? 1 : 0);
+  int ids_next = load_ids(64);
+  int next_chunk = 1;                        // chunk held in `ids_next`
+  auto issue = [&](int k, Regs& R) {
+    const bool real = k < nreal;
+    load_block(__builtin_amdgcn_readlane(ids, real ? (k & 63) : 0), real, R);
+  };
+  auto done = [&](int k) {                   // block k reduced; k + NBUF is issued next
+    if (((k + NBUF) & 63) == 0 && k + NBUF < nreal) {
+      ids = ids_next;
+      ++next_chunk;
+      ids_next = load_ids(next_chunk * 64);
+    }
+  };
+  std::integral_constant<bool, false> full;
+  Regs R[NBUF];
+  issue(0, R[0]);
+  for (int k = 0; k < nfull; k += NBUF) {
+#pragma unroll
+    for (int s = 0; s < NBUF; ++s) {
+      issue(k + s + 1, R[(s + 1) % NBUF]);
       __builtin_amdgcn_sched_barrier(0);
-      if (k + 1 < nmine) process_block(full, B, kBlockTokens);
+      if (s == 0 || k + s < nfull) {
+        process_block(full, R[s], kBlockTokens);
+        done(k + s);
+      }
     }
   }
-  // The partial last block (only in a sequence's last partition).
-  const int tail = ntok - nfull * kBlockTokens;
-  if (tail > 0 && w == nfull % kWaves) {
-    Regs T;
-    load_block(nfull, true, T);
-    process_block(std::integral_constant<bool, true>(), T, tail);
+  if (tail > 0) {
+    std::integral_constant<bool, true> last;
+    if (nfull & 1)
+      process_block(last, R[1], tail);
+    else
+      process_block(last, R[0], tail);
   }
+  finalize();
+}
 
-  // Merge the RPW row groups of this wave.
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    float M = m[hh];
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float f = fast_exp2(m[hh] - ((M == kNegInf) ? 0.f : M));
-    float lw = l[hh] * f;
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float o = acc[hh][e] * f;
-#pragma unroll
-      for (int off = LPR; off < 64; off <<= 1) o += __shfl_xor(o, off);
-      acc[hh][e] = o;
-    }
-    m[hh] = M;
-    l[hh] = lw;
-  }
-
-  // Merge the waves through LDS (reusing the block-id area).
-  __syncthreads();
-  float* s_m = smem;                          // [kWaves][G]
-  float* s_l = s_m + kWaves * G;              // [kWaves][G]
-  float* s_o = s_l + kWaves * G;              // [kWaves][G][D]
-  int* s_bad = reinterpret_cast<int*>(s_o + kWaves * G * D);   // [kWaves]
-  if (r == 0) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[(w * G + hh) * D + c * 8 + e] = acc[hh][e];
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      s_m[w * G + hh] = m[hh];
-      s_l[w * G + hh] = l[hh];
-    }
-    s_bad[w] = bad_blk ? 1 : 0;
-  }
-  __syncthreads();
-  const bool any_bad = s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3];
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int hh = i / D, d = i % D;
-    float M = s_m[hh];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww * G + hh]);
-    const float Mu = (M == kNegInf) ? 0.f : M;
-    float den = 0.f, num = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = fast_exp2(s_m[ww * G + hh] - Mu);
-      den = fmaf(s_l[ww * G + hh], f, den);
-      num = fmaf(s_o[(ww * G + hh) * D + d], f, num);
-    }
-    if (any_bad) {
-      num = den = M = __builtin_nanf("");
-    }
-    const size_t row = (size_t)b * Hq + h0 + hh;
-    if (p.direct) {
-      p.out[row * D + d] = f32_to_f16_bits(num / den);
-      if (d == 0 && p.lse) p.lse[row] = (M + __log2f(den)) * kLn2;
-    } else {
-      const size_t rec = row * p.n_part + part;
-      p.part_o[rec * D + d] = num;
-      if (d == 0) p.part_ml[rec] = make_float2(M, den);
-    }
-  }
+// Waves (kv heads) per workgroup: four when the heads divide evenly.
+int waves_per_group(const DecodeParams& p) {
+  return (p.kv_heads % 4 == 0) ? 4 : (p.kv_heads % 2 == 0) ? 2 : 1;
 }
 
 template <int D, int G, bool I8>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
-  const int max_ids = p.partition_size / kBlockTokens;
-  const size_t lds_ids = (size_t)max_ids * sizeof(int);
-  const size_t lds_merge = (size_t)kWaves * G * (D + 2) * sizeof(float) + kWaves * sizeof(int);
-  const size_t lds = lds_ids > lds_merge ? lds_ids : lds_merge;
-  const unsigned grid = (unsigned)p.n_part * p.batch * p.kv_heads;
-  hipLaunchKernelGGL((decode_valu_kernel<D, G, I8>), dim3(grid), dim3(kThreads), lds, stream, p);
+  const int wpg = waves_per_group(p);
+  const unsigned grid = (unsigned)p.n_part * p.batch * (p.kv_heads / wpg);
+  hipLaunchKernelGGL((decode_valu_kernel<D, G, I8>), dim3(grid), dim3(64 * wpg), 0, stream, p);
   return hipGetLastError();
 }
 

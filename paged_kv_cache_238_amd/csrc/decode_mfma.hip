@@ -190,9 +190,13 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int L = p.context_lens[b];
   const int row_left = p.max_blocks - j0;
   const int span_blocks = span * (P / kBlockTokens);
-  auto load_ids = [&](int c0) {              // block ids c0 .. c0+63 of the span
-    const int cnt = min(min(span_blocks, row_left) - c0, 64);
-    return (lane < cnt) ? bt_row[j0 + c0 + lane] : 0;
+  // Block ids c0 .. c0+63 of the run, one per lane, through a buffer
+  // resource bounded to the run's slice of the table row: ids past the
+  // slice read as 0 with no branch, so the load stays asynchronous.
+  const __amdgpu_buffer_rsrc_t rids =
+      make_rsrc(bt_row + j0, (uint32_t)max(min(span_blocks, row_left), 0) * 4u);
+  auto load_ids = [&](int c0) {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(rids, (uint32_t)(c0 + lane) * 4u, 0, 0);
   };
   int ids = load_ids(0);
 
@@ -433,30 +437,32 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
   };
 
-  // Full blocks of the span, streamed in order.  Block ids come one per
-  // lane from a 64-block chunk (the next chunk's ids are fetched when a
-  // chunk starts).  Register sets rotate so that NBUF - 1 blocks are in
-  // flight while one is reduced (int8 blocks are half the bytes, so they go
-  // one deeper); prefetches past the end read nothing.  Every branch is
+  // Full blocks of the run, streamed in order.  Block ids come one per lane
+  // from `ids`, a 64-block chunk; the following chunk is fetched into
+  // `ids_next` a whole chunk ahead and moved over just before its first
+  // block is issued, so no issue reads a register whose load may still be
+  // pending.  Register sets rotate so that NBUF - 1 blocks are in flight
+  // while one is reduced (int8 blocks are half the bytes, so they go one
+  // deeper); prefetches past the end read nothing.  Every branch is
   // wave-uniform and no load sits inside one, so the waits stay exact.
+  constexpr int NBUF = I8 ? PA_MFMA_NBUF_I8 : PA_MFMA_NBUF_F16;
   std::integral_constant<bool, false> full;
+  // The chunk of the partial last block is moved in too, so its id is in `ids`.
+  const int nreal = nfull + (tail > 0 ? 1 : 0);
   int ids_next = load_ids(64);
-  int id_chunk = 0;                          // chunk held in `ids`
+  int next_chunk = 1;                        // chunk held in `ids_next`
   auto issue = [&](int k, Regs& R) {
     const bool real = k < nfull;
-    const int kk = real ? k : 0;
-    const int src = (kk >> 6) == id_chunk ? ids : ids_next;
-    load_block(__builtin_amdgcn_readlane(src, kk & 63), real, R);
+    load_block(__builtin_amdgcn_readlane(ids, real ? (k & 63) : 0), real, R);
   };
-  auto done = [&](int k) {                   // block k reduced
-    if (((k + 1) & 63) == 0) {               // leave chunk k >> 6
+  auto done = [&](int k) {                   // block k reduced; k + NBUF is issued next
+    if (((k + NBUF) & 63) == 0 && k + NBUF < nreal) {
       ids = ids_next;
-      ++id_chunk;
-      ids_next = load_ids((id_chunk + 1) * 64);
+      ++next_chunk;
+      ids_next = load_ids(next_chunk * 64);
     }
   };
   if (nfull > 0) {
-    constexpr int NBUF = I8 ? PA_MFMA_NBUF_I8 : PA_MFMA_NBUF_F16;
     Regs R[NBUF];
 #pragma unroll
     for (int s = 0; s + 1 < NBUF; ++s) issue(s, R[s]);
@@ -472,10 +478,10 @@ void decode_mfma_kernel(const DecodeParams p) {
       }
     }
   }
-  // The partial last block (only in a sequence's last partition).
+  // The partial last block (only in a sequence's last run).
   if (tail > 0) {
     Regs T;
-    load_block(bt_row[j0 + nfull], true, T);
+    load_block(__builtin_amdgcn_readlane(ids, nfull & 63), true, T);
     process_block(std::integral_constant<bool, true>(), T, tail);
   }
   finalize();

@@ -10,14 +10,16 @@ namespace {
 
 using pa::kBlockTokens;
 
-constexpr int kDefaultPartition = 512;      // smallest automatic partition (tokens)
-constexpr int kMatrixPartition = 256;       // matrix-core kernel's split granularity
-constexpr int kMaxAutoPartition = 4096;     // largest automatic partition
-constexpr long long kMinWorkgroups = 2048;  // 256 CUs x 8
-// Matrix-core kernel: runs are lengthened while at least this many remain
-// (256 CUs x 8 waves, two four-wave workgroups per CU).
-constexpr long long kTargetWaves = 2048;
-constexpr int kMaxPartition = 1 << 18;      // block ids of one partition fit LDS
+// Split granularity of both decode kernels (tokens).  A wave streams a run
+// of consecutive partitions, sized on the device from the actual lengths
+// (run_span.h), so the partition only sets the finest split.
+constexpr int kRunPartition = 256;
+// Runs are lengthened while at least this many remain over the batch
+// (256 CUs x 8 waves).
+#ifndef PA_TARGET_WAVES
+#define PA_TARGET_WAVES 2048
+#endif
+constexpr int kMaxPartition = 1 << 18;      // largest partition accepted (tokens)
 constexpr float kLog2e = 1.4426950408889634f;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -42,24 +44,17 @@ int check_decode_shapes(int max_blocks, int max_context_len, int batch, int q_he
   return PA_OK;
 }
 
-// Library's partition size.  Matrix-core kernel (groups of 4+): 256 tokens;
-// it merges runs of partitions per wave, sized on the device from the
-// actual lengths, so the partition only sets the finest split.  VALU kernel: start at 512 tokens and double
-// (up to 4096) while the grid would still hold at least kMinWorkgroups
-// workgroups; a partition there costs a fixed prologue (block ids, Q) and
-// epilogue (cross-wave merge, record store), so larger partitions win as
-// long as every CU keeps several workgroups.
-int resolve_partition(int batch, int q_heads, int kv_heads, int head_dim, int max_context_len,
-                      int partition_size) {
-  (void)head_dim;
+// Library's partition size: the caller's if given.  Otherwise, when the
+// (sequence, kv head) pairs alone reach the wave target, one
+// partition covering the longest context (no split, no merge); else
+// kRunPartition, with runs sized on the device.
+int resolve_partition(int batch, int kv_heads, int max_context_len, int partition_size) {
   if (partition_size > 0) return partition_size;
-  if (kv_heads > 0 && q_heads / kv_heads >= 4) return kMatrixPartition;
-  const long long pairs = (long long)batch * kv_heads;
-  int P = kDefaultPartition;
-  while (P < kMaxAutoPartition &&
-         pairs * ((max_context_len + 2LL * P - 1) / (2LL * P)) >= kMinWorkgroups)
-    P *= 2;
-  return P;
+  if ((long long)batch * kv_heads >= PA_TARGET_WAVES) {
+    const int whole = (max(max_context_len, 1) + kBlockTokens - 1) / kBlockTokens * kBlockTokens;
+    if (whole <= kMaxPartition) return max(whole, kRunPartition);
+  }
+  return kRunPartition;
 }
 
 int num_partitions(int max_context_len, int P) {
@@ -99,8 +94,7 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   int st = check_decode_shapes(max_blocks, max_context_len, batch, q_heads, kv_heads, head_dim,
                                block_size, num_blocks, partition_size);
   if (st != PA_OK) return st;
-  const int P = resolve_partition(batch, q_heads, kv_heads, head_dim, max_context_len,
-                                  partition_size);
+  const int P = resolve_partition(batch, kv_heads, max_context_len, partition_size);
   const int n_part = num_partitions(max_context_len, P);
   if ((long long)n_part * batch * kv_heads > INT_MAX) return PA_ERR_SHAPE;   // 1-D grids
   const bool direct = (mode == 0 && n_part == 1);
@@ -136,7 +130,7 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   p.n_part = n_part;
   p.scale_log2 = scale * kLog2e;
   p.direct = direct ? 1 : 0;
-  p.target_waves = (int)kTargetWaves;
+  p.target_waves = PA_TARGET_WAVES;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = status_of(pa::launch_decode(p, int8, s));
   if (st != PA_OK || direct || mode == 1) return st;
@@ -234,7 +228,7 @@ int pa_decode_partition_size(int batch, int q_heads, int kv_heads, int head_dim,
   if (check_decode_shapes(1 << 30 >> 4, max_context_len, batch, q_heads, kv_heads, head_dim,
                           kBlockTokens, 1, partition_size) != PA_OK)
     return 0;
-  return resolve_partition(batch, q_heads, kv_heads, head_dim, max_context_len, partition_size);
+  return resolve_partition(batch, kv_heads, max_context_len, partition_size);
 }
 
 size_t pa_decode_workspace_size(int batch, int q_heads, int kv_heads, int head_dim,

@@ -30,7 +30,7 @@ struct DecodeParams {
   int n_part;                 // ceil(max_context_len / partition_size)
   float scale_log2;           // scale * log2(e)
   int direct;                 // 1: n_part == 1, write out/lse directly
-  int target_waves;           // matrix-core kernel: run-length target (run_span.h)
+  int target_waves;           // run-length target (run_span.h)
   int* header;                // split mode: workspace header; [0] = run span
 };
 

@@ -1,4 +1,4 @@
-// Run length of the matrix-core decode kernel, computed on the device from
+// Run length of the decode kernels, computed on the device from
 // the actual context lengths, identically by the partition kernel and the
 // merge kernel.
 //
