@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra steps timed one by one with L2 and MALL flushed before "
+                         "each (reported under 'cold'; 0 to skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the "
                          "known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -163,6 +166,51 @@ class Case:
         wall = time.perf_counter() - t0
         kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
         return wall, kern_ms
+
+    def run_cold(self, steps, flush_bytes=1 << 30):
+        """Steps with the caches flushed before each: a 1 GiB buffer (beyond
+        the 256 MB MALL and the 8 x 4 MB of L2) is read, outside the timed
+        events.  Reading rather than zeroing leaves no dirty lines whose
+        write-back would land inside the timed step.  Returns sorted step and
+        decode-kernel times (ms)."""
+        torch = self.torch
+        flush = torch.ones(flush_bytes // 8, dtype=torch.int64, device=self.v["q"].device)
+        step_ms, kern_ms = [], []
+        for _ in range(steps):
+            flush.sum()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+            self.write()
+            e[1].record()
+            self.decode_kernel()
+            e[2].record()
+            self.merge()
+            e[3].record()
+            torch.cuda.synchronize()
+            step_ms.append(e[0].elapsed_time(e[3]))
+            kern_ms.append(e[1].elapsed_time(e[2]))
+        del flush
+        return sorted(step_ms), sorted(kern_ms)
+
+
+def cold_summary(case, steps):
+    """Median and p10/p90 of cold steps (caches flushed before each)."""
+    if steps <= 0:
+        return None
+    step_ms, kern_ms = case.run_cold(steps)
+
+    def pick(v, q):
+        return v[min(len(v) - 1, int(q * len(v)))]
+    step_med = pick(step_ms, 0.5) / 1e3
+    kern_med = pick(kern_ms, 0.5) / 1e3
+    return {
+        "steps": steps,
+        "step_us_median": round(step_med * 1e6, 2),
+        "step_us_p10_p90": [round(pick(step_ms, 0.1) * 1e3, 2), round(pick(step_ms, 0.9) * 1e3, 2)],
+        "step_GBps": round(case.kv_bytes / step_med / 1e9, 1),
+        "decode_kernel_us_median": round(kern_med * 1e6, 2),
+        "decode_kernel_GBps": round(case.kv_bytes / kern_med / 1e9, 1),
+    }
 
 
 def summarize(case, wall, kern_ms, steps):
@@ -318,14 +366,20 @@ def main():
     head = Case(pa, torch, gen, args.workload, args.partition_size, dev)
     wall, kern = head.run(args.steps, args.warmup)
     s = summarize(head, wall, kern, args.steps)
+    s["cold"] = cold_summary(head, args.cold_steps)
     print(f"[bench] {args.workload}: {s['ms_per_step']} ms/step, decode kernel "
           f"{s['decode_kernel_us_mean']} us = {s['decode_kernel_GBps']} GB/s", file=sys.stderr,
           flush=True)
+    if s["cold"]:
+        print(f"[bench] {args.workload} cold: step {s['cold']['step_us_median']} us, decode "
+              f"kernel {s['cold']['decode_kernel_us_median']} us = "
+              f"{s['cold']['decode_kernel_GBps']} GB/s", file=sys.stderr, flush=True)
     others = []
     for name in [n for n in args.others.split(",") if n and n != args.workload]:
         c = Case(pa, torch, gen, name, -1, dev)
         w2, k2 = c.run(max(20, args.steps // 2), max(5, args.warmup // 2))
         o = summarize(c, w2, k2, max(20, args.steps // 2))
+        o["cold"] = cold_summary(c, args.cold_steps)
         others.append(o)
         print(f"[bench] {name}: {o['ms_per_step']} ms/step, decode kernel "
               f"{o['decode_kernel_us_mean']} us = {o['decode_kernel_GBps']} GB/s",
@@ -360,6 +414,7 @@ def main():
                      "launch_us_mean": s["decode_kernel_us_mean"],
                      "traffic": traffic_for(args.workload),
                      "source_hash": source_hash()},
+        "cold": s["cold"],
         "cpu_baseline": cpu,
         "others": others,
     }

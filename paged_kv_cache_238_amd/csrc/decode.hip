@@ -125,20 +125,18 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   const int r = lane / LPR, c = lane % LPR;
   const int Hq = p.q_heads, Hkv = p.kv_heads;
 
-  // 1-D grid, run index slowest: consecutive workgroups (dealt round-robin
-  // to the eight XCDs) are the head groups and sequences of one run index.
+  // Workgroup item = (run, head group), assigned on the device over the
+  // real runs only, in contiguous shares per XCD (locate_run).
   const int groups = Hkv / wpg;
-  const int per_run = p.batch * groups;
-  const int ridx = blockIdx.x / per_run;
-  const int rem = blockIdx.x % per_run;
-  const int b = rem / groups;
-  const int g = (rem % groups) * wpg + w;
+  const RunSlot rs = locate_run(p, groups);
+  const int span = rs.span;
+  const int g = rs.grp * wpg + w;
   const int h0 = g * G;
+  if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = span;
+  if (rs.b < 0) return;                      // past the last run
+  const int b = rs.b, ridx = rs.ridx;
 
   const int P = p.partition_size;
-  const int span = p.direct ? 1 : run_span(p.context_lens, p.batch, Hkv, p.max_context_len, P,
-                                           p.target_waves);
-  if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = span;
   const int t_begin = ridx * span * P;
   const int j0 = min(t_begin / kBlockTokens, p.max_blocks - 1);
   const int32_t* bt_row = p.block_table + (size_t)b * p.max_blocks;
@@ -433,7 +431,7 @@ int waves_per_group(const DecodeParams& p) {
 template <int D, int G, bool I8>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   const int wpg = waves_per_group(p);
-  const unsigned grid = (unsigned)p.n_part * p.batch * (p.kv_heads / wpg);
+  const unsigned grid = decode_workgroups(p, wpg);
   hipLaunchKernelGGL((decode_valu_kernel<D, G, I8>), dim3(grid), dim3(64 * wpg), 0, stream, p);
   return hipGetLastError();
 }

@@ -161,23 +161,18 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int li = lane & 15;       // index in group: token row for loads, head for softmax
   const int Hq = p.q_heads, Hkv = p.kv_heads;
 
-  // 1-D grid, run index slowest: consecutive workgroups (dealt round-robin
-  // to the eight XCDs) are the head groups and sequences of one run index,
-  // so every XCD gets an even share even when lengths differ.  A wave
-  // streams run `ridx` (partitions [ridx*span, (ridx+1)*span)) of its head
-  // and merges it online into one record.
+  // Workgroup item = (run, head group), assigned on the device over the
+  // real runs only, in contiguous shares per XCD (locate_run).
   const int groups = Hkv / wpg;
-  const int per_run = p.batch * groups;
-  const int ridx = blockIdx.x / per_run;
-  const int rem = blockIdx.x % per_run;
-  const int b = rem / groups;
-  const int g = (rem % groups) * wpg + w;
+  const RunSlot rs = locate_run(p, groups);
+  const int span = rs.span;
+  const int g = rs.grp * wpg + w;
   const int h0 = g * G;
+  if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = span;
+  if (rs.b < 0) return;                      // past the last run
+  const int b = rs.b, ridx = rs.ridx;
 
   const int P = p.partition_size;
-  const int span = p.direct ? 1 : run_span(p.context_lens, p.batch, Hkv, p.max_context_len, P,
-                                           p.target_waves);
-  if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = span;
   const int part0 = ridx * span;             // first partition of this run
   const int t_begin = part0 * P;
   const int j0 = min(t_begin / kBlockTokens, p.max_blocks - 1);
@@ -501,8 +496,7 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   using Geo = Geometry<D, I8>;
   const int wpg = waves_per_group(p);
   const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes;
-  // runs never outnumber partitions, so n_part bounds the run index
-  const unsigned grid = (unsigned)p.n_part * p.batch * (p.kv_heads / wpg);
+  const unsigned grid = decode_workgroups(p, wpg);
   hipLaunchKernelGGL((decode_mfma_kernel<D, G, I8>), dim3(grid), dim3(64 * wpg), lds, stream, p);
   return hipGetLastError();
 }

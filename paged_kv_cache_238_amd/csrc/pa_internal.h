@@ -30,7 +30,7 @@ struct DecodeParams {
   int n_part;                 // ceil(max_context_len / partition_size)
   float scale_log2;           // scale * log2(e)
   int direct;                 // 1: n_part == 1, write out/lse directly
-  int target_waves;           // run-length target (run_span.h)
+  int target_waves;           // run-length target (locate_run, run_span.h)
   int* header;                // split mode: workspace header; [0] = run span
 };
 
@@ -56,6 +56,20 @@ struct WriteParams {
   int num_tokens, kv_heads, head_dim;
   long long capacity;         // num_blocks * 16 slots
 };
+
+// Workgroups of a decode launch with `wpg` kv heads per workgroup: one per
+// sequence in direct mode; otherwise the number of (run, head group)
+// items, bounded on the host (locate_run in run_span.h): at most
+// n_part * batch * kv_heads / wpg, and fewer than 2 * target_waves / wpg
+// when batch * kv_heads is below the target.
+inline unsigned decode_workgroups(const DecodeParams& p, int wpg) {
+  const long long groups = p.kv_heads / wpg;
+  if (p.direct) return (unsigned)(p.batch * groups);
+  const long long full = (long long)p.n_part * p.batch * groups;
+  if ((long long)p.batch * p.kv_heads >= p.target_waves) return (unsigned)full;
+  const long long bound = (2LL * p.target_waves + wpg - 1) / wpg;
+  return (unsigned)(full < bound ? full : bound);
+}
 
 // Launchers return hipSuccess or the launch error.  `int8` selects the
 // int8-cache instantiation.

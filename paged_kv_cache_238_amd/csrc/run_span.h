@@ -1,48 +1,121 @@
-// Run length of the decode kernels, computed on the device from
-// the actual context lengths, identically by the partition kernel and the
-// merge kernel.
+// Work assignment of the decode kernels, computed on the device from the
+// actual context lengths by every workgroup (the merge kernel reads the run
+// length back from the workspace header).
 //
 // Partitions are the split granularity; one wave streams a run of `span`
-// consecutive partitions of one (sequence, kv head) and merges them online
+// consecutive partitions of one (sequence, kv head) and merges it online
 // (the running-max rescaling is itself an exact log-sum-exp merge), so one
-// record covers a run.  span is the largest power of two that still leaves
-// at least `target_waves` runs over the whole batch:
+// record covers a run.  span is the largest power of two (at most the
+// longest sequence's partition count) that still leaves at least
+// `target_waves` runs over the whole batch:
 //   sum_b ceil(n_b / span) * kv_heads >= target_waves,  n_b = ceil(L_b / P).
 // Long sequences therefore get long runs, and a batch of short or mixed
-// lengths keeps span 1.  When batch * kv_heads alone reaches the target no
-// length is read and span is 1.
+// lengths keeps span 1.  When batch * kv_heads alone reaches the target,
+// span is 1.
+//
+// Items are (run, head group) pairs over the real runs only, in the order
+// (run index, sequence, head group): first run 0 of every sequence, then
+// run 1 of every sequence that has one, and so on; workgroup i takes item
+// i.  Run index k is held by the c_k sequences with more than k runs, so
+// cum(k) = sum_b min(runs_b, k) runs precede level k.  With uniform lengths
+// this is simply run-index-major order; consecutive workgroups, dealt
+// round-robin to the eight XCDs, are different sequences and head groups of
+// the same run index.  (Measured on MI355X, this order streams faster than
+// sequence-major or per-XCD contiguous orders of the same runs.)
+//
+// Whenever batch * kv_heads is below the target there are fewer than
+// 2 * target_waves runs times kv_heads: either span = 1 and runs(1) <=
+// 2 runs(2) < 2 T / kv_heads, or span = s >= 2 is the last power of two
+// meeting the target, and runs(s) <= 2 runs(2s) < 2 T / kv_heads or (2s
+// past the longest sequence) every sequence has at most 2 runs.  The host
+// sizes the grid by that bound; workgroups left without an item exit.
 #pragma once
 
 #include "pa_internal.h"
 
 namespace pa {
 
-// Must be called by all 64 lanes of a wave; the result is wave-uniform.
-__device__ inline int run_span(const int32_t* context_lens, int batch, int kv_heads,
-                               int max_context_len, int partition_size, int target_waves) {
-  if ((long long)batch * kv_heads >= target_waves) return 1;
+struct RunSlot {
+  int span;   // partitions per run
+  int b;      // sequence, or -1: no item for this workgroup
+  int ridx;   // run index within the sequence
+  int grp;    // head group (kv heads grp*wpg .. grp*wpg+wpg-1)
+};
+
+__device__ inline int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+__device__ inline int wave_max(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off));
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Item of this workgroup.  Must be called by all 64 lanes of each wave; the
+// result is wave-uniform.  In direct mode (one partition covers every
+// context) the runs are the sequences themselves, empty or invalid ones
+// included: the kernel writes their rows.
+__device__ inline RunSlot locate_run(const DecodeParams& p, int groups) {
+  RunSlot r{1, -1, 0, (int)(blockIdx.x % groups)};
+  const int item = blockIdx.x / groups;      // run number, head groups fastest
+  if (p.direct) {
+    if (item < p.batch) r.b = item;
+    return r;
+  }
   const int lane = threadIdx.x & 63;
-  const int max_part = (max_context_len + partition_size - 1) / partition_size;
+  const int P = p.partition_size;
+  const int max_part = (p.max_context_len + P - 1) / P;
   auto parts = [&](int b) {                  // partitions of sequence b (0 if invalid)
-    if (b >= batch) return 0;
-    const int L = context_lens[b];
-    return (L > 0 && L <= max_context_len) ? (L + partition_size - 1) / partition_size : 0;
+    if (b >= p.batch) return 0;
+    const int L = p.context_lens[b];
+    return (L > 0 && L <= p.max_context_len) ? (L + P - 1) / P : 0;
   };
   const int n0 = parts(lane);                // batches of up to 64 need one load
+  auto parts_of = [&](int b0) { return b0 == 0 ? n0 : parts(b0 + lane); };
   int span = 1;
-  for (int s = 2; s <= max_part; s *= 2) {
-    long long runs = 0;
-    for (int b0 = 0; b0 < batch; b0 += 64) {
-      const int n = b0 == 0 ? n0 : parts(b0 + lane);
-      int r = (n + s - 1) / s;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) r += __shfl_xor(r, off);
-      runs += r;
+  if ((long long)p.batch * p.kv_heads < p.target_waves) {
+    for (int s = 2; s <= max_part; s *= 2) {
+      long long runs = 0;
+      for (int b0 = 0; b0 < p.batch; b0 += 64) runs += wave_sum((parts_of(b0) + s - 1) / s);
+      if (runs * p.kv_heads < p.target_waves) break;
+      span = s;
     }
-    if (runs * kv_heads < target_waves) break;
-    span = s;
   }
-  return __builtin_amdgcn_readfirstlane(span);
+  r.span = span = __builtin_amdgcn_readfirstlane(span);
+  auto runs_of = [&](int b0) { return (parts_of(b0) + span - 1) / span; };
+
+  // cum(k): runs at indices below k over the batch
+  auto cum = [&](int k) {
+    long long c = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64) c += wave_sum(min(runs_of(b0), k));
+    return c;
+  };
+  int max_r = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += 64) max_r = max(max_r, wave_max(runs_of(b0)));
+  if (item >= cum(max_r)) return r;          // past the last run
+  int lo = 0, hi = max_r - 1;                // largest k with cum(k) <= item
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cum(mid) <= item) lo = mid; else hi = mid - 1;
+  }
+  long long rank = item - cum(lo);           // among the sequences with more than lo runs
+  for (int b0 = 0; b0 < p.batch; b0 += 64) {
+    const unsigned long long has = __ballot(runs_of(b0) > lo);
+    const int cnt = (int)__builtin_popcountll(has);
+    if (rank < cnt) {
+      const unsigned below = __builtin_amdgcn_mbcnt_hi((unsigned)(has >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((unsigned)has, 0u));
+      const bool mine = ((has >> lane) & 1ull) && below == (unsigned)rank;
+      r.b = b0 + (int)__builtin_ctzll(__ballot(mine));
+      r.ridx = lo;
+      return r;
+    }
+    rank -= cnt;
+  }
+  return r;                                  // not reached
 }
 
 }  // namespace pa

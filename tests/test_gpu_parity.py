@@ -387,3 +387,28 @@ def test_long_context_eight_head_workgroups(pa, int8):
     out = gpu_decode(pa, wl, d, partition_size=512, return_lse=False)
     want, _ = oracle_decode(wl, vals)
     check_close(out.cpu().numpy(), want, f"long ctx int8={int8}")
+
+
+@pytest.mark.parametrize("G,int8", [(1, False), (2, True), (8, False), (8, True)])
+def test_runs_enumerated_over_many_sequences(pa, G, int8):
+    """More than 64 sequences of mixed lengths (several 64-lane chunks in the
+    device-side run numbering), with empty and one-token sequences; at the
+    library's partition and at 16 tokens, where runs of several partitions
+    form."""
+    over = dict(batch=150, q_heads=G * 2, kv_heads=2, head_dim=64, lmin=1, lmax=3000,
+                occupancy=0.9, kv_dtype="int8" if int8 else "fp16")
+    wl = gen.make("gqa70b_mixed", seed=700 + G + int8, overrides=over)
+    wl.context_lens[[5, 70, 149]] = 0
+    wl.context_lens[[6, 130]] = [1, 3000]
+    wl = _rebuild_table(wl)
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    d = device_inputs(wl, vals)
+    want, want_lse = oracle_decode(wl, vals)
+    live = wl.context_lens > 0
+    for P in (0, 16):
+        say(f"many sequences G={G} int8={int8} P={P} B={wl.batch}")
+        out, lse = gpu_decode(pa, wl, d, partition_size=P)
+        out, lse = out.cpu().numpy(), lse.cpu().numpy()
+        assert not out[~live].any() and np.all(np.isneginf(lse[~live]))
+        check_close(out[live], want[live], f"many sequences G={G} int8={int8} P={P}")
+        np.testing.assert_allclose(lse[live], want_lse[live], rtol=0, atol=1e-4)
