@@ -67,7 +67,7 @@ inline unsigned decode_workgroups(const DecodeParams& p, int wpg) {
   if (p.direct) return (unsigned)(p.batch * groups);
   const long long full = (long long)p.n_part * p.batch * groups;
   if ((long long)p.batch * p.kv_heads >= p.target_waves) return (unsigned)full;
-  const long long bound = (2LL * p.target_waves + wpg - 1) / wpg;
+  const long long bound = ((long long)p.target_waves + wpg - 1) / wpg;
   return (unsigned)(full < bound ? full : bound);
 }
 

@@ -75,14 +75,22 @@ __device__ inline RunSlot locate_run(const DecodeParams& p, int groups) {
   };
   const int n0 = parts(lane);                // batches of up to 64 need one load
   auto parts_of = [&](int b0) { return b0 == 0 ? n0 : parts(b0 + lane); };
+  // span: the smallest run length (in partitions) that leaves at most
+  // target_waves (run, kv head) items; items(s) does not grow with s, and at
+  // s = max_part every sequence is one run (batch * kv_heads < target).
+  auto items = [&](int s) {
+    long long runs = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64) runs += wave_sum((parts_of(b0) + s - 1) / s);
+    return runs * p.kv_heads;
+  };
   int span = 1;
-  if ((long long)p.batch * p.kv_heads < p.target_waves) {
-    for (int s = 2; s <= max_part; s *= 2) {
-      long long runs = 0;
-      for (int b0 = 0; b0 < p.batch; b0 += 64) runs += wave_sum((parts_of(b0) + s - 1) / s);
-      if (runs * p.kv_heads < p.target_waves) break;
-      span = s;
+  if ((long long)p.batch * p.kv_heads < p.target_waves && items(1) > p.target_waves) {
+    int lo = 1, hi = max_part;               // items(lo) > target >= items(hi)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (items(mid) <= p.target_waves) hi = mid; else lo = mid;
     }
+    span = hi;
   }
   r.span = span = __builtin_amdgcn_readfirstlane(span);
   auto runs_of = [&](int b0) { return (parts_of(b0) + span - 1) / span; };
