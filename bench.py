@@ -12,7 +12,10 @@ partitions).  Inputs are seeded synthetic tensors already resident in HBM.
 Headline workload: one Llama2-7B-shaped layer - 32 sequences x 4096 tokens,
 32 query / 32 kv heads, head_dim 128, fp16, 16-token blocks, block tables 85 %
 contiguous.  metric value = ideal KV bytes / step time (GB/s); the other
-workloads are measured the same way and reported under "others".
+workloads are measured the same way and reported under "others"; the
+shared-prefix workload is measured twice, through pa_decode and through the
+shared-prefix entry point (whose "decode call" time covers its three
+kernels).  "cold" repeats steps one at a time with L2 and MALL flushed first.
 
 "roofline" describes the dominant kernel (the decode partition kernel):
 achieved = its algorithmic bytes (the KV bytes it must read) / its mean
@@ -55,6 +58,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="run the workload through the shared-prefix entry point "
+                         "(workloads with a shared prefix only)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed one by one with L2 and MALL flushed before "
                          "each (reported under 'cold'; 0 to skip)")
@@ -91,8 +97,9 @@ def decode_kernel_name(wl) -> str:
 class Case:
     """Device-resident inputs of one workload plus its step."""
 
-    def __init__(self, pa, torch, gen, name, partition_size, dev):
+    def __init__(self, pa, torch, gen, name, partition_size, dev, shared_prefix=0):
         self.pa, self.torch, self.name = pa, torch, name
+        self.shared_prefix = shared_prefix          # > 0: shared-prefix path, prefix tokens
         wl = gen.make(name, poison=False)
         self.wl = wl
         vals = gen.fill_torch(wl, dev)
@@ -106,6 +113,10 @@ class Case:
         self.n_part = max(1, -(-wl.max_context_len // self.P))
         need = pa.workspace_size(wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim,
                                  wl.max_context_len, self.P)
+        if shared_prefix:
+            need = pa.shared_prefix_workspace_size(wl.batch, wl.q_heads, wl.kv_heads,
+                                                   wl.head_dim, wl.max_context_len,
+                                                   shared_prefix)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         self.out = torch.empty_like(vals["q"])
         self.int8 = wl.kv_dtype == "int8"
@@ -124,7 +135,14 @@ class Case:
         """The partition kernel alone: direct output when one partition
         covers the context, else the partition records."""
         v, wl = self.v, self.wl
-        if self.n_part == 1:
+        if self.shared_prefix:
+            # the whole entry point: suffix partition kernel, prefix kernel, merge
+            self.pa.decode_shared_prefix(v["q"], v["k_pool"], v["v_pool"], self.bt, self.cl,
+                                         self.shared_prefix, scale=wl.scale,
+                                         max_context_len=wl.max_context_len, out=self.out,
+                                         workspace=self.ws, k_scale=v.get("k_scale"),
+                                         v_scale=v.get("v_scale"))
+        elif self.n_part == 1:
             if self.int8:
                 self.pa.decode_int8(v["q"], v["k_pool"], v["v_pool"], v["k_scale"], v["v_scale"],
                                     self.bt, self.cl, scale=wl.scale, partition_size=self.P,
@@ -141,7 +159,7 @@ class Case:
                                     k_scale=v.get("k_scale"), v_scale=v.get("v_scale"))
 
     def merge(self):
-        if self.n_part > 1:
+        if self.n_part > 1 and not self.shared_prefix:
             wl = self.wl
             self.pa.merge_partials(self.ws, self.cl, wl.q_heads, wl.head_dim, self.P,
                                    wl.max_context_len, out=self.out)
@@ -219,7 +237,8 @@ def summarize(case, wall, kern_ms, steps):
     kmean = sum(kern_ms) / len(kern_ms) / 1e3
     med = kern_ms[len(kern_ms) // 2] / 1e3
     return {
-        "workload": wl.name, "batch": wl.batch, "q_heads": wl.q_heads, "kv_heads": wl.kv_heads,
+        "workload": wl.name + (" (shared-prefix path)" if case.shared_prefix else ""),
+        "batch": wl.batch, "q_heads": wl.q_heads, "kv_heads": wl.kv_heads,
         "head_dim": wl.head_dim, "block_size": 16, "kv_dtype": wl.kv_dtype,
         "max_context_len": wl.max_context_len,
         "mean_context_len": round(float(wl.context_lens.mean()), 1),
@@ -363,7 +382,10 @@ def main():
     from workloads import gen
 
     dev = torch.device("cuda:0")
-    head = Case(pa, torch, gen, args.workload, args.partition_size, dev)
+    pre = gen.SPECS[args.workload].get("prefix", 0) if args.shared_prefix else 0
+    if args.shared_prefix and not pre:
+        raise SystemExit(f"--shared-prefix: workload {args.workload} has no shared prefix")
+    head = Case(pa, torch, gen, args.workload, args.partition_size, dev, shared_prefix=pre)
     wall, kern = head.run(args.steps, args.warmup)
     s = summarize(head, wall, kern, args.steps)
     s["cold"] = cold_summary(head, args.cold_steps)
@@ -386,6 +408,18 @@ def main():
               file=sys.stderr, flush=True)
         del c
         torch.cuda.empty_cache()
+        if name == "prefix_shared":
+            # the same workload through the shared-prefix entry point
+            c = Case(pa, torch, gen, name, -1, dev, shared_prefix=gen.SPECS[name]["prefix"])
+            w2, k2 = c.run(max(20, args.steps // 2), max(5, args.warmup // 2))
+            o = summarize(c, w2, k2, max(20, args.steps // 2))
+            o["cold"] = cold_summary(c, args.cold_steps)
+            others.append(o)
+            print(f"[bench] {o['workload']}: {o['ms_per_step']} ms/step, decode call "
+                  f"{o['decode_kernel_us_mean']} us = {o['decode_kernel_GBps']} GB/s",
+                  file=sys.stderr, flush=True)
+            del c
+            torch.cuda.empty_cache()
     cpu = None if args.no_cpu_baseline else cpu_baseline(head, args.cpu_seconds)
     achieved = s["decode_kernel_GBps"]
     line = {

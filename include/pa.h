@@ -191,10 +191,10 @@ int pa_decode_int8(void* out, float* lse_out, const void* q, const int8_t* k_poo
  *                                       record.  Record r of (b, h) covers
  *                                       partitions [r*span, (r+1)*span).
  *                                       span is chosen on the device from
- *                                       the context lengths: the largest
- *                                       power of two that leaves at least
- *                                       2048 (record, kv head) runs over
- *                                       the batch (1 when batch * kv_heads
+ *                                       the context lengths: the smallest
+ *                                       span that leaves at most 2048
+ *                                       (record, kv head) runs over the
+ *                                       batch (1 when batch * kv_heads
  *                                       alone reaches 2048); one wave
  *                                       merges a run's partitions online.
  *   float2 ml[batch][q_heads][n_part]   (m, l): m = a reference point in
@@ -230,6 +230,59 @@ int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,
                       int max_context_len, int batch, int q_heads, int head_dim,
                       int partition_size, const void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * Shared-prefix decode.  The adg.csdn.net article on ATB's KV Cache
+ * management (section "Prefix Caching") keeps one copy of the KV of a
+ * prefix common to many requests (a system prompt), and the zskr.cn article
+ * on ATB's PagedAttention (section "踩坑二") has those pages referenced by
+ * every request that shares them.  pa_decode reads such a page once per
+ * referencing sequence; these entry points read each shared page once per
+ * kv head for all sequences together: the queries of all sequences (for kv
+ * head g, the G query heads of every sequence) form 16-query tiles against
+ * the shared keys on the matrix cores, giving one (max, sum, output) record
+ * per (sequence, query head, prefix partition) - partitions of 16 to 256
+ * tokens, sized so that the prefix kernel runs about 1024 waves; the private
+ * suffixes [prefix_len, L_b) are decoded as by pa_decode_partials; one
+ * log-sum-exp merge combines both record sets.  The result is the same
+ * attention as pa_decode (up to rounding order).
+ *
+ *   prefix_len       tokens of the shared prefix: a positive multiple of 16,
+ *                    at most max_context_len.
+ *   block_table      as for pa_decode; caller contract: for every b,
+ *                    block_table[b][j] == block_table[0][j] for
+ *                    j < prefix_len / 16 (the prefix ids are read from row
+ *                    0 only) and context_lens[b] >= prefix_len.  A sequence
+ *                    with context_lens[b] < prefix_len or > max_context_len
+ *                    gets NaN rows.
+ *   workspace        pa_decode_shared_prefix_workspace_size(...) bytes,
+ *                    required (the split always runs).
+ *   all other arguments as for pa_decode / pa_decode_int8; the suffixes use
+ *   the library's 256-token partitions.
+ *
+ * Returns PA_ERR_SHAPE for a bad prefix_len, otherwise the codes of
+ * pa_decode.  Launches, in order on `stream`: the suffix partition kernel,
+ * the prefix kernel and the merge kernel.
+ */
+size_t pa_decode_shared_prefix_workspace_size(int batch, int q_heads, int kv_heads,
+                                              int head_dim, int max_context_len,
+                                              int prefix_len);
+
+int pa_decode_shared_prefix(void* out, float* lse_out, const void* q, const void* k_pool,
+                            const void* v_pool, const int32_t* block_table, int max_blocks,
+                            const int32_t* context_lens, int max_context_len, int batch,
+                            int q_heads, int kv_heads, int head_dim, int block_size,
+                            int num_blocks, float scale, int prefix_len, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+int pa_decode_shared_prefix_int8(void* out, float* lse_out, const void* q, const int8_t* k_pool,
+                                 const int8_t* v_pool, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_table,
+                                 int max_blocks, const int32_t* context_lens,
+                                 int max_context_len, int batch, int q_heads, int kv_heads,
+                                 int head_dim, int block_size, int num_blocks, float scale,
+                                 int prefix_len, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

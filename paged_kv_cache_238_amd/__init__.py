@@ -12,7 +12,8 @@ Functions mirror the C entry points:
   decode(q, k_pool, v_pool, block_table, context_lens, ...)
   decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, ...)
   decode_partials(...), decode_partials_int8(...), merge_partials(...)
-  workspace_size(...), partition_size(...)
+  decode_shared_prefix(q, k_pool, v_pool, block_table, context_lens, prefix_len, ...)
+  workspace_size(...), partition_size(...), shared_prefix_workspace_size(...)
 """
 from __future__ import annotations
 
@@ -23,7 +24,8 @@ import os
 __all__ = [
     "PaError", "LIB_PATH", "lib", "status_string", "write_kv", "write_kv_int8",
     "partition_size", "workspace_size", "decode", "decode_int8", "decode_partials",
-    "decode_partials_int8", "merge_partials", "EXPORTS",
+    "decode_partials_int8", "merge_partials", "decode_shared_prefix",
+    "shared_prefix_workspace_size", "EXPORTS",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,6 +65,11 @@ EXPORTS = {
     "pa_decode_partials_int8": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
                                      _i, _f, _i, _p, _z, _p]),
     "pa_merge_partials": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _z, _p]),
+    "pa_decode_shared_prefix_workspace_size": (_z, [_i, _i, _i, _i, _i, _i]),
+    "pa_decode_shared_prefix": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
+                                     _i, _f, _i, _p, _z, _p]),
+    "pa_decode_shared_prefix_int8": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i,
+                                          _i, _i, _i, _i, _f, _i, _p, _z, _p]),
 }
 for _name, (_res, _args) in EXPORTS.items():
     _fn = getattr(lib, _name)
@@ -295,4 +302,41 @@ def merge_partials(workspace, context_lens, q_heads, head_dim, partition_size, m
     _check(lib.pa_merge_partials(_ptr(out), _ptr(lse), _ptr(context_lens), int(max_context_len),
                                  B, q_heads, head_dim, int(partition_size), _ptr(workspace),
                                  nbytes, _stream(context_lens)), "pa_merge_partials")
+    return (out, lse) if return_lse else out
+
+
+def shared_prefix_workspace_size(batch, q_heads, kv_heads, head_dim, max_context_len,
+                                 prefix_len) -> int:
+    return int(lib.pa_decode_shared_prefix_workspace_size(batch, q_heads, kv_heads, head_dim,
+                                                          max_context_len, prefix_len))
+
+
+def decode_shared_prefix(q, k_pool, v_pool, block_table, context_lens, prefix_len, scale=None,
+                         max_context_len=None, out=None, return_lse=False, workspace=None,
+                         k_scale=None, v_scale=None):
+    """Decode where every sequence's first `prefix_len` tokens sit in the same
+    blocks (row 0's ids); the shared blocks are read once per kv head for all
+    sequences.  int8 pools when k_scale / v_scale are given."""
+    torch = _torch()
+    int8 = k_scale is not None
+    B, Hq, Hkv, D, NB, bs, MB, L = _decode_args(
+        q, k_pool, v_pool, block_table, context_lens, torch.int8 if int8 else torch.float16,
+        max_context_len, k_scale, v_scale)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out, lse = _alloc_out(q, out, return_lse)
+    need = shared_prefix_workspace_size(B, Hq, Hkv, D, L, int(prefix_len))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    if int8:
+        _check(lib.pa_decode_shared_prefix_int8(
+            _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+            _ptr(v_scale), _ptr(block_table), MB, _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB,
+            scale, int(prefix_len), _ptr(workspace), nbytes, _stream(q)),
+            "pa_decode_shared_prefix_int8")
+    else:
+        _check(lib.pa_decode_shared_prefix(
+            _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), MB,
+            _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB, scale, int(prefix_len),
+            _ptr(workspace), nbytes, _stream(q)), "pa_decode_shared_prefix")
     return (out, lse) if return_lse else out

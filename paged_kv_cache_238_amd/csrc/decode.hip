@@ -139,11 +139,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   const int P = p.partition_size;
   const int t_begin = ridx * span * P;
   const int j0 = min(t_begin / kBlockTokens, p.max_blocks - 1);
-  const int32_t* bt_row = p.block_table + (size_t)b * p.max_blocks;
+  const int32_t* bt_row =
+      p.block_table + (size_t)b * p.bt_stride + p.token_offset / kBlockTokens;
 
   // Start-up loads, all independent: length, first 64 block ids of the run
   // (clamped to the table row), Q.
-  const int L = p.context_lens[b];
+  const int L = p.context_lens[b] - p.token_offset;
   const int row_left = p.max_blocks - j0;
   const int span_blocks = span * (P / kBlockTokens);
   // Block ids c0 .. c0+63 of the run, one per lane, through a buffer

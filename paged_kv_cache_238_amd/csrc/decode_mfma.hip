@@ -143,7 +143,7 @@ struct Geometry {
 // whole partition and writes its own record.  The waves of a workgroup thus
 // read neighbouring slices of the same token rows at the same time, and a
 // wave's start-up (length, block ids, Q) is paid once per partition.
-template <int D, int G, bool I8>
+template <int D, int G, bool I8, bool PREFIX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES_PER_EU)))
 void decode_mfma_kernel(const DecodeParams p) {
   using Geo = Geometry<D, I8>;
@@ -162,27 +162,51 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int Hq = p.q_heads, Hkv = p.kv_heads;
 
   // Workgroup item = (run, head group), assigned on the device over the
-  // real runs only, in contiguous shares per XCD (locate_run).
+  // real runs only, in contiguous shares per XCD (locate_run).  Shared
+  // prefix: item = (query tile, run, head group), head groups fastest; the
+  // stream is table row 0 over the prefix, one partition per run.
   const int groups = Hkv / wpg;
-  const RunSlot rs = locate_run(p, groups);
-  const int span = rs.span;
-  const int g = rs.grp * wpg + w;
+  int grp, b, ridx, span, tile = 0;
+  if constexpr (PREFIX) {
+    const int n_rg = p.n_part * groups;
+    tile = blockIdx.x / n_rg;
+    ridx = (blockIdx.x % n_rg) / groups;
+    grp = blockIdx.x % groups;
+    b = 0;
+    span = 1;
+  } else {
+    const RunSlot rs = locate_run(p, groups);
+    span = rs.span;
+    grp = rs.grp;
+    if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = span;
+    if (rs.b < 0) return;                    // past the last run
+    b = rs.b;
+    ridx = rs.ridx;
+  }
+  const int g = grp * wpg + w;
   const int h0 = g * G;
-  if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = span;
-  if (rs.b < 0) return;                      // past the last run
-  const int b = rs.b, ridx = rs.ridx;
+  // Row of q / out / records of query slot li, or -1 for a padding slot.
+  int qrow = -1;
+  if constexpr (PREFIX) {
+    const int Gm = Hq / Hkv;
+    const int qi = tile * 16 + li;
+    if (qi < p.batch * Gm) qrow = (qi / Gm) * Hq + g * Gm + qi % Gm;
+  } else {
+    if (li < G) qrow = b * Hq + h0 + li;
+  }
 
   const int P = p.partition_size;
   const int part0 = ridx * span;             // first partition of this run
   const int t_begin = part0 * P;
   const int j0 = min(t_begin / kBlockTokens, p.max_blocks - 1);
-  const int32_t* bt_row = p.block_table + (size_t)b * p.max_blocks;
+  const int32_t* bt_row =
+      p.block_table + (size_t)b * p.bt_stride + p.token_offset / kBlockTokens;
 
   // Start-up loads, all independent: the length, the first 64 block ids of
   // the run (clamped to the table row; only those below the length are
   // used) and Q.  Block ids live one per lane and are read back with
   // v_readlane, so the table slice is fetched once per wave.
-  const int L = p.context_lens[b];
+  const int L = PREFIX ? p.max_context_len : p.context_lens[b] - p.token_offset;
   const int row_left = p.max_blocks - j0;
   const int span_blocks = span * (P / kBlockTokens);
   // Block ids c0 .. c0+63 of the run, one per lane, through a buffer
@@ -195,32 +219,31 @@ void decode_mfma_kernel(const DecodeParams p) {
   };
   int ids = load_ids(0);
 
-  // Q^T as the B operand of the QK product: lane holds Q[h0 + li][dim(kk, lg, j)].
+  // Q^T as the B operand of the QK product: lane holds Q[slot li][dim(kk, lg, j)].
   // Each step's 8 dims are consecutive (Geo::dim), so one 16-byte load each;
-  // padding heads (li >= G) load head 0 and are zeroed.
+  // padding slots load row 0 and are zeroed.
   h8 qB[NKK];
   {
-    const bool real_head = li < G;
-    const uint16_t* qrow = p.q + ((size_t)b * Hq + h0 + (real_head ? li : 0)) * D;
+    const uint16_t* qsrc = p.q + (size_t)(qrow >= 0 ? qrow : 0) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      uint4 v = *reinterpret_cast<const uint4*>(qrow + Geo::dim(kk, lg, 0));
-      if (!real_head) v = make_uint4(0, 0, 0, 0);
+      uint4 v = *reinterpret_cast<const uint4*>(qsrc + Geo::dim(kk, lg, 0));
+      if (qrow < 0) v = make_uint4(0, 0, 0, 0);
       qB[kk] = __builtin_bit_cast(h8, v);
     }
   }
 
   if (L < 0 || L > p.max_context_len) {      // broken metadata: NaN rows
-    if (ridx == 0 && p.direct && li < G) {
-      const size_t row = (size_t)b * Hq + h0 + li;
+    if (ridx == 0 && p.direct && qrow >= 0) {
+      const size_t row = (size_t)qrow;
       for (int d = lg; d < D; d += 4) p.out[row * D + d] = 0x7E00;
       if (lg == 0 && p.lse) p.lse[row] = __builtin_nanf("");
     }
     return;
   }
   if (t_begin >= L) {                        // empty run (L == 0: zero row)
-    if (p.direct && ridx == 0 && li < G) {
-      const size_t row = (size_t)b * Hq + h0 + li;
+    if (p.direct && ridx == 0 && qrow >= 0) {
+      const size_t row = (size_t)qrow;
       for (int d = lg; d < D; d += 4) p.out[row * D + d] = 0;
       if (lg == 0 && p.lse) p.lse[row] = kNegInf;
     }
@@ -402,8 +425,8 @@ void decode_mfma_kernel(const DecodeParams p) {
     float den = l_run;
     den += __shfl_xor(den, 16);
     den += __shfl_xor(den, 32);
-    if (li < G) {
-      const size_t row = (size_t)b * Hq + h0 + li;
+    if (qrow >= 0) {
+      const size_t row = (size_t)qrow;
       float M = m_run;
       if (bad_blk) M = den = __builtin_nanf("");
       if (p.direct) {
@@ -497,7 +520,21 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   const int wpg = waves_per_group(p);
   const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes;
   const unsigned grid = decode_workgroups(p, wpg);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, G, I8>), dim3(grid), dim3(64 * wpg), lds, stream, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G, I8, false>), dim3(grid), dim3(64 * wpg), lds,
+                     stream, p);
+  return hipGetLastError();
+}
+
+// Shared prefix: (query tile, prefix partition, head group) workgroups of up
+// to four kv heads.
+template <int D, bool I8>
+hipError_t launch_prefix(const DecodeParams& p, hipStream_t stream) {
+  using Geo = Geometry<D, I8>;
+  const int wpg = (p.kv_heads % 4 == 0) ? 4 : (p.kv_heads % 2 == 0) ? 2 : 1;
+  const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes;
+  const unsigned grid = (unsigned)((long long)p.prefix_tiles * p.n_part * (p.kv_heads / wpg));
+  hipLaunchKernelGGL((decode_mfma_kernel<D, 16, I8, true>), dim3(grid), dim3(64 * wpg), lds,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -512,6 +549,12 @@ hipError_t dispatch_group(const DecodeParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_prefix_mfma(const DecodeParams& p, bool int8, hipStream_t stream) {
+  if (p.head_dim == 128) return int8 ? launch_prefix<128, true>(p, stream) : launch_prefix<128, false>(p, stream);
+  if (p.head_dim == 64) return int8 ? launch_prefix<64, true>(p, stream) : launch_prefix<64, false>(p, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode_mfma(const DecodeParams& p, bool int8, hipStream_t stream) {
   if (p.head_dim == 128)

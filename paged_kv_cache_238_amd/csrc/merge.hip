@@ -14,6 +14,10 @@
 // into D/4 float4 columns x (1024/D) partition phases; each lane sums its
 // phase's partitions, then the phases are added through LDS in a fixed
 // order (deterministic).
+//
+// Shared-prefix decode merges two record sets per row: the runs over the
+// private suffix [prefix, L) and n_pre records over the shared prefix;
+// both enter the same sums (the log-sum-exp merge is associative).
 #include "pa_internal.h"
 
 namespace pa {
@@ -39,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, col = tid % COLS, ph = tid / COLS;
   const size_t row = (size_t)b * p.q_heads + h;
-  const int L = p.context_lens[b];
+  const int L = p.context_lens[b] - p.token_offset;
 
   if (L < 0 || L > p.max_context_len) {
     for (int d = tid; d < D; d += kThreads) p.out[row * D + d] = 0x7E00;
@@ -49,7 +53,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   // records cover runs of `span` partitions (written by the partition kernel)
   const int span = max(1, p.header[0]);
   const int n_part_b = (L + p.partition_size - 1) / p.partition_size;
-  const int n = (n_part_b + span - 1) / span;
+  const int n_suf = (n_part_b + span - 1) / span;
+  const int n_pre = p.pre_ml ? p.n_pre : 0;
+  const int n = n_suf + n_pre;               // records: suffix runs, then prefix
   if (n == 0) {
     for (int d = tid; d < D; d += kThreads) p.out[row * D + d] = 0;
     if (tid == 0 && p.lse) p.lse[row] = kNegInf;
@@ -57,10 +63,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   }
   const float2* ml = p.part_ml + row * p.n_part;
   const float4* o = reinterpret_cast<const float4*>(p.part_o + row * p.n_part * D);
+  const float2* ml2 = n_pre ? p.pre_ml + row * n_pre : nullptr;
+  const float4* o2 = n_pre ? reinterpret_cast<const float4*>(p.pre_o + row * n_pre * D) : nullptr;
+  auto rec_ml = [&](int i) { return i < n_suf ? ml[i] : ml2[i - n_suf]; };
+  auto rec_o = [&](int i) {
+    return i < n_suf ? o[(size_t)i * COLS + col] : o2[(size_t)(i - n_suf) * COLS + col];
+  };
 
   // M = max_p m_p
   float M = kNegInf;
-  for (int i = tid; i < n; i += kThreads) M = fmaxf(M, ml[i].x);
+  for (int i = tid; i < n; i += kThreads) M = fmaxf(M, rec_ml(i).x);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   if ((tid & 63) == 0) s_max[tid >> 6] = M;
@@ -73,10 +85,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.f;
   for (int i = ph; i < n; i += PH) {
-    const float2 r = ml[i];
+    const float2 r = rec_ml(i);
     const float wgt = __builtin_amdgcn_exp2f(r.x - Mu);
     den = fmaf(wgt, r.y, den);
-    const float4 v = o[(size_t)i * COLS + col];
+    const float4 v = rec_o(i);
     acc.x = fmaf(wgt, v.x, acc.x);
     acc.y = fmaf(wgt, v.y, acc.y);
     acc.z = fmaf(wgt, v.z, acc.z);

@@ -120,6 +120,7 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   p.part_ml = direct ? nullptr : reinterpret_cast<float2*>(ws + rec.ml_offset);
   p.part_o = direct ? nullptr : reinterpret_cast<float*>(ws + rec.o_offset);
   p.max_blocks = max_blocks;
+  p.bt_stride = max_blocks;
   p.max_context_len = max_context_len;
   p.batch = batch;
   p.q_heads = q_heads;
@@ -148,6 +149,142 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   mp.partition_size = P;
   mp.n_part = n_part;
   mp.max_context_len = max_context_len;
+  return status_of(pa::launch_merge(mp, s));
+}
+
+// Shared-prefix workspace: [header][suffix (m, l) and o records, n_suf per
+// row][prefix (m, l) records, n_pre per row][prefix o records].
+struct PrefixRecords {
+  Records suf;
+  size_t pre_ml, pre_o, total;
+};
+
+PrefixRecords prefix_layout(int batch, int q_heads, int head_dim, int n_suf, int n_pre) {
+  PrefixRecords r;
+  r.suf = record_layout(batch, q_heads, head_dim, n_suf);
+  const size_t n = (size_t)batch * q_heads * n_pre;
+  r.pre_ml = align_up(r.suf.total, 256);
+  r.pre_o = align_up(r.pre_ml + n * sizeof(float2), 256);
+  r.total = r.pre_o + n * head_dim * sizeof(float);
+  return r;
+}
+
+// Partition of the shared prefix: short enough that the prefix kernel has
+// about PA_PREFIX_WAVES waves ((query tile, partition, kv head) items), at
+// least one block, at most kRunPartition.  Its waves stream few blocks each
+// and are latency-bound, so more of them win over fewer, longer ones.
+#ifndef PA_PREFIX_WAVES
+#define PA_PREFIX_WAVES 1024
+#endif
+int prefix_partition(int batch, int q_heads, int kv_heads, int prefix_len) {
+  const long long tiles = ((long long)batch * (q_heads / kv_heads) + 15) / 16;
+  const long long per_part = tiles * kv_heads;   // waves per partition
+  long long P = (long long)prefix_len * per_part / PA_PREFIX_WAVES;
+  P = P / kBlockTokens * kBlockTokens;
+  if (P < kBlockTokens) P = kBlockTokens;
+  if (P > kRunPartition) P = kRunPartition;
+  return (int)P;
+}
+
+int check_prefix(int max_context_len, int prefix_len) {
+  if (prefix_len <= 0 || prefix_len % kBlockTokens != 0 || prefix_len > max_context_len)
+    return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+// Decode over a prefix of prefix_len tokens shared by every sequence (table
+// row 0's first prefix_len / 16 ids) plus each sequence's own suffix:
+// partials over the suffixes, records over the prefix for all queries at
+// once, then one merge of both.
+int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
+                  const void* v_pool, const float* k_scale, const float* v_scale, bool int8,
+                  const int32_t* block_table, int max_blocks, const int32_t* context_lens,
+                  int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
+                  int block_size, int num_blocks, float scale, int prefix_len, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens) return PA_ERR_NULL;
+  if (int8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  int st = check_decode_shapes(max_blocks, max_context_len, batch, q_heads, kv_heads, head_dim,
+                               block_size, num_blocks, 0);
+  if (st != PA_OK) return st;
+  if ((st = check_prefix(max_context_len, prefix_len)) != PA_OK) return st;
+  const int P = kRunPartition;
+  const int suf_max = max_context_len - prefix_len;
+  const int n_suf = num_partitions(suf_max, P);
+  const int P_pre = prefix_partition(batch, q_heads, kv_heads, prefix_len);
+  const int n_pre = num_partitions(prefix_len, P_pre);
+  const long long queries = (long long)batch * (q_heads / kv_heads);
+  const int tiles = (int)((queries + 15) / 16);
+  if ((long long)n_suf * batch * kv_heads > INT_MAX ||
+      (long long)tiles * n_pre * kv_heads > INT_MAX)
+    return PA_ERR_SHAPE;
+  const PrefixRecords rec = prefix_layout(batch, q_heads, head_dim, n_suf, n_pre);
+  if (!workspace) return PA_ERR_NULL;
+  if (workspace_bytes < rec.total) return PA_ERR_WORKSPACE;
+  if (batch == 0) return PA_OK;
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pa::DecodeParams p = {};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.batch = batch;
+  p.q_heads = q_heads;
+  p.kv_heads = kv_heads;
+  p.head_dim = head_dim;
+  p.num_blocks = num_blocks;
+  p.partition_size = P;
+  p.scale_log2 = scale * kLog2e;
+  p.target_waves = PA_TARGET_WAVES;
+  p.bt_stride = max_blocks;
+
+  // Suffixes [prefix_len, L_b): run records, as pa_decode_partials would
+  // write them for the shifted sequences.
+  pa::DecodeParams ps = p;
+  ps.header = reinterpret_cast<int*>(ws);
+  ps.part_ml = reinterpret_cast<float2*>(ws + rec.suf.ml_offset);
+  ps.part_o = reinterpret_cast<float*>(ws + rec.suf.o_offset);
+  ps.token_offset = prefix_len;
+  ps.max_blocks = max_blocks - prefix_len / kBlockTokens;
+  ps.max_context_len = suf_max;
+  ps.n_part = n_suf;
+  st = status_of(pa::launch_decode(ps, int8, s));
+  if (st != PA_OK) return st;
+
+  // Prefix: one record per (sequence, query head, prefix partition).
+  pa::DecodeParams pp = p;
+  pp.part_ml = reinterpret_cast<float2*>(ws + rec.pre_ml);
+  pp.part_o = reinterpret_cast<float*>(ws + rec.pre_o);
+  pp.max_blocks = prefix_len / kBlockTokens;
+  pp.max_context_len = prefix_len;
+  pp.partition_size = P_pre;
+  pp.n_part = n_pre;
+  pp.prefix_tiles = tiles;
+  st = status_of(pa::launch_prefix_mfma(pp, int8, s));
+  if (st != PA_OK) return st;
+
+  pa::MergeParams mp = {};
+  mp.header = ps.header;
+  mp.part_ml = ps.part_ml;
+  mp.part_o = ps.part_o;
+  mp.context_lens = context_lens;
+  mp.out = static_cast<uint16_t*>(out);
+  mp.lse = lse_out;
+  mp.batch = batch;
+  mp.q_heads = q_heads;
+  mp.head_dim = head_dim;
+  mp.partition_size = P;
+  mp.n_part = n_suf;
+  mp.max_context_len = suf_max;
+  mp.token_offset = prefix_len;
+  mp.pre_ml = pp.part_ml;
+  mp.pre_o = pp.part_o;
+  mp.n_pre = n_pre;
   return status_of(pa::launch_merge(mp, s));
 }
 
@@ -284,6 +421,46 @@ int pa_decode_partials_int8(const void* q, const int8_t* k_pool, const int8_t* v
                        block_table, max_blocks, context_lens, max_context_len, batch, q_heads,
                        kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
                        workspace, workspace_bytes, stream);
+}
+
+size_t pa_decode_shared_prefix_workspace_size(int batch, int q_heads, int kv_heads,
+                                              int head_dim, int max_context_len,
+                                              int prefix_len) {
+  if (check_decode_shapes(1 << 30 >> 4, max_context_len, batch, q_heads, kv_heads, head_dim,
+                          kBlockTokens, 1, 0) != PA_OK ||
+      check_prefix(max_context_len, prefix_len) != PA_OK)
+    return 0;
+  return prefix_layout(batch, q_heads, head_dim,
+                       num_partitions(max_context_len - prefix_len, kRunPartition),
+                       num_partitions(prefix_len,
+                                      prefix_partition(batch, q_heads, kv_heads, prefix_len)))
+      .total;
+}
+
+int pa_decode_shared_prefix(void* out, float* lse_out, const void* q, const void* k_pool,
+                            const void* v_pool, const int32_t* block_table, int max_blocks,
+                            const int32_t* context_lens, int max_context_len, int batch,
+                            int q_heads, int kv_heads, int head_dim, int block_size,
+                            int num_blocks, float scale, int prefix_len, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return prefix_common(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_table,
+                       max_blocks, context_lens, max_context_len, batch, q_heads, kv_heads,
+                       head_dim, block_size, num_blocks, scale, prefix_len, workspace,
+                       workspace_bytes, stream);
+}
+
+int pa_decode_shared_prefix_int8(void* out, float* lse_out, const void* q, const int8_t* k_pool,
+                                 const int8_t* v_pool, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_table,
+                                 int max_blocks, const int32_t* context_lens,
+                                 int max_context_len, int batch, int q_heads, int kv_heads,
+                                 int head_dim, int block_size, int num_blocks, float scale,
+                                 int prefix_len, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return prefix_common(out, lse_out, q, k_pool, v_pool, k_scale, v_scale, true, block_table,
+                       max_blocks, context_lens, max_context_len, batch, q_heads, kv_heads,
+                       head_dim, block_size, num_blocks, scale, prefix_len, workspace,
+                       workspace_bytes, stream);
 }
 
 int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,

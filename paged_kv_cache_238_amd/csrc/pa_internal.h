@@ -23,8 +23,12 @@ struct DecodeParams {
   float* lse;                 // fp32 [B, Hq] or null (direct mode)
   float2* part_ml;            // [B, Hq, n_part] (split mode)
   float* part_o;              // [B, Hq, n_part, D] (split mode)
-  int max_blocks;
-  int max_context_len;
+  int max_blocks;             // table entries per row from token_offset on
+  int bt_stride;              // table row stride (entries)
+  int token_offset;           // tokens [0, token_offset) of every sequence are
+                              // skipped (multiple of 16): lengths and table rows
+                              // are read past them
+  int max_context_len;        // bound on context_lens - token_offset
   int batch, q_heads, kv_heads, head_dim, num_blocks;
   int partition_size;         // tokens, multiple of 16
   int n_part;                 // ceil(max_context_len / partition_size)
@@ -32,6 +36,11 @@ struct DecodeParams {
   int direct;                 // 1: n_part == 1, write out/lse directly
   int target_waves;           // run-length target (locate_run, run_span.h)
   int* header;                // split mode: workspace header; [0] = run span
+  // Shared-prefix mode (matrix-core kernel): the stream is table row 0 over
+  // max_context_len tokens (the prefix), one partition per run, and the 16
+  // query slots of a wave are queries of different sequences: query
+  // qi = tile * 16 + slot is head g * G + qi % G of sequence qi / G.
+  int prefix_tiles;           // ceil(batch * G / 16)
 };
 
 struct MergeParams {
@@ -43,6 +52,12 @@ struct MergeParams {
   float* lse;
   int batch, q_heads, head_dim;
   int partition_size, n_part, max_context_len;
+  int token_offset;           // records cover tokens [token_offset, L)
+  // Optional second record set (shared prefix): n_pre records per row, all
+  // present.  Null when absent.
+  const float2* pre_ml;
+  const float* pre_o;
+  int n_pre;
 };
 
 struct WriteParams {
@@ -60,8 +75,8 @@ struct WriteParams {
 // Workgroups of a decode launch with `wpg` kv heads per workgroup: one per
 // sequence in direct mode; otherwise the number of (run, head group)
 // items, bounded on the host (locate_run in run_span.h): at most
-// n_part * batch * kv_heads / wpg, and fewer than 2 * target_waves / wpg
-// when batch * kv_heads is below the target.
+// n_part * batch * kv_heads / wpg, and at most target_waves / wpg when
+// batch * kv_heads is below the target.
 inline unsigned decode_workgroups(const DecodeParams& p, int wpg) {
   const long long groups = p.kv_heads / wpg;
   if (p.direct) return (unsigned)(p.batch * groups);
@@ -77,6 +92,8 @@ inline unsigned decode_workgroups(const DecodeParams& p, int wpg) {
 hipError_t launch_decode(const DecodeParams& p, bool int8, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, bool int8, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, bool int8, hipStream_t stream);
+// Shared prefix: records of every (sequence, query head) over the prefix.
+hipError_t launch_prefix_mfma(const DecodeParams& p, bool int8, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_write_kv(const WriteParams& p, hipStream_t stream);
 hipError_t launch_write_kv_int8(const WriteParams& p, hipStream_t stream);

@@ -5,13 +5,14 @@
 // Partitions are the split granularity; one wave streams a run of `span`
 // consecutive partitions of one (sequence, kv head) and merges it online
 // (the running-max rescaling is itself an exact log-sum-exp merge), so one
-// record covers a run.  span is the largest power of two (at most the
-// longest sequence's partition count) that still leaves at least
-// `target_waves` runs over the whole batch:
-//   sum_b ceil(n_b / span) * kv_heads >= target_waves,  n_b = ceil(L_b / P).
-// Long sequences therefore get long runs, and a batch of short or mixed
-// lengths keeps span 1.  When batch * kv_heads alone reaches the target,
-// span is 1.
+// record covers a run.  span is the smallest whole number of partitions
+// that leaves at most `target_waves` (run, kv head) items over the batch:
+//   items(span) = sum_b ceil(n_b / span) * kv_heads <= target_waves,
+//   n_b = ceil(L_b / P);
+// items(s) does not grow with s, so it is found by bisection.  Long
+// sequences therefore get long runs, and a batch of short or mixed lengths
+// keeps span 1.  When batch * kv_heads alone reaches the target, span is 1
+// (the library then normally picks one partition per sequence instead).
 //
 // Items are (run, head group) pairs over the real runs only, in the order
 // (run index, sequence, head group): first run 0 of every sequence, then
@@ -21,14 +22,10 @@
 // this is simply run-index-major order; consecutive workgroups, dealt
 // round-robin to the eight XCDs, are different sequences and head groups of
 // the same run index.  (Measured on MI355X, this order streams faster than
-// sequence-major or per-XCD contiguous orders of the same runs.)
-//
-// Whenever batch * kv_heads is below the target there are fewer than
-// 2 * target_waves runs times kv_heads: either span = 1 and runs(1) <=
-// 2 runs(2) < 2 T / kv_heads, or span = s >= 2 is the last power of two
-// meeting the target, and runs(s) <= 2 runs(2s) < 2 T / kv_heads or (2s
-// past the longest sequence) every sequence has at most 2 runs.  The host
-// sizes the grid by that bound; workgroups left without an item exit.
+// sequence-major or per-XCD contiguous orders of the same runs.)  There are
+// at most target_waves / wpg items of wpg-head workgroups when batch *
+// kv_heads is below the target; the host launches that many workgroups and
+// those left without an item exit.
 #pragma once
 
 #include "pa_internal.h"
@@ -70,7 +67,7 @@ __device__ inline RunSlot locate_run(const DecodeParams& p, int groups) {
   const int max_part = (p.max_context_len + P - 1) / P;
   auto parts = [&](int b) {                  // partitions of sequence b (0 if invalid)
     if (b >= p.batch) return 0;
-    const int L = p.context_lens[b];
+    const int L = p.context_lens[b] - p.token_offset;
     return (L > 0 && L <= p.max_context_len) ? (L + P - 1) / P : 0;
   };
   const int n0 = parts(lane);                // batches of up to 64 need one load

@@ -97,3 +97,55 @@ def test_merge_validation():
     assert f(FAKE, None, FAKE, 1000, 2, 8, 128, 0, FAKE, 1 << 30, None) == UNSUP
     assert f(FAKE, None, FAKE, 1000, 2, 8, 128, 512, FAKE, 10, None) == WS
     assert f(None, None, FAKE, 1000, 2, 8, 128, 512, FAKE, 1 << 30, None) == NULL
+
+
+def test_partition_choice():
+    # 256-token partitions while batch * kv_heads is below 2048 waves ...
+    assert pa.partition_size(32, 32, 32, 128, 4096, 0) == 256
+    assert pa.partition_size(4, 64, 8, 128, 131072, 0) == 256
+    # ... one partition covering the longest context once it reaches 2048
+    assert pa.partition_size(64, 32, 32, 128, 1530, 0) == 1536
+    assert pa.partition_size(64, 32, 32, 128, 100, 0) == 256
+    assert pa.workspace_size(64, 32, 32, 128, 1530, 0) == 256 + 64 * 32 * (8 + 512)
+
+
+def spd(**kw):
+    a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=96, cl=FAKE, mcl=1536,
+             B=64, Hq=32, Hkv=32, D=128, bs=16, NB=1200, scale=0.1, pre=1024, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return pa.lib.pa_decode_shared_prefix(a["out"], a["lse"], a["q"], a["k"], a["v"], a["bt"],
+                                          a["mb"], a["cl"], a["mcl"], a["B"], a["Hq"], a["Hkv"],
+                                          a["D"], a["bs"], a["NB"], a["scale"], a["pre"], a["ws"],
+                                          a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pre=0), SHAPE), (dict(pre=-16), SHAPE), (dict(pre=1000), SHAPE),
+    (dict(pre=1552), SHAPE), (dict(out=None), NULL), (dict(ws=None), NULL),
+    (dict(wsb=1000), WS), (dict(Hq=24, Hkv=1), UNSUP), (dict(D=80), UNSUP),
+])
+def test_shared_prefix_validation(kw, code):
+    assert spd(**kw) == code
+
+
+def test_shared_prefix_workspace_size():
+    # header; suffix records over ceil((1536 - 1024) / 256) = 2 partitions;
+    # prefix records: 4 query tiles x 32 kv heads = 128 waves per prefix
+    # partition, so 128-token partitions (about 1024 waves), 8 of them;
+    # 256-byte aligned parts
+    rows = 64 * 32
+    suf = 256 + rows * 2 * 8 + rows * 2 * 512
+    assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
+        suf + rows * 8 * 8 + rows * 8 * 512
+    assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1000) == 0
+    assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1024, 1024) == \
+        256 + rows * (8 + 512) + rows * 8 * (8 + 512)
+    # few queries: 2 tiles x 8 kv heads = 16 waves per partition, so the
+    # smallest partition (one block), 64 of them
+    assert pa.shared_prefix_workspace_size(4, 64, 8, 128, 1024, 1024) == \
+        256 + 4 * 64 * (8 + 512) + 4 * 64 * 64 * (8 + 512)
+    # many queries: 64 tiles x 32 heads = 2048 waves per partition -> 256 tokens
+    # (the largest)
+    assert pa.shared_prefix_workspace_size(1024, 32, 32, 64, 1024, 1024) == \
+        256 + 1024 * 32 * (8 + 256) + 1024 * 32 * 4 * (8 + 256)

@@ -1,0 +1,140 @@
+"""GPU parity of the shared-prefix decode (pa_decode_shared_prefix /
+pa_decode_shared_prefix_int8) against the CPU fp64 oracle.
+
+Shared-prefix decode computes the same attention as pa_decode: the oracle is
+ref_decode on the same inputs, and the gates are those of pa_decode
+(max|gpu - ref| <= 1e-2, relative RMS <= 1e-3)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+from workloads import gen
+
+from test_gpu_parity import (DEV, _host_copy, check_close, device_inputs, oracle_decode, say,
+                             t)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    import paged_kv_cache_238_amd as m
+    return m
+
+
+def run_prefix(pa, wl, d, prefix_len, return_lse=True):
+    if wl.kv_dtype == "int8":
+        return pa.decode_shared_prefix(d["q"], d["k_pool"], d["v_pool"], d["block_table"],
+                                       d["context_lens"], prefix_len, scale=wl.scale,
+                                       max_context_len=wl.max_context_len,
+                                       return_lse=return_lse, k_scale=d["k_scale"],
+                                       v_scale=d["v_scale"])
+    return pa.decode_shared_prefix(d["q"], d["k_pool"], d["v_pool"], d["block_table"],
+                                   d["context_lens"], prefix_len, scale=wl.scale,
+                                   max_context_len=wl.max_context_len, return_lse=return_lse)
+
+
+def prefix_len_of(wl):
+    """Length of the prefix every table row shares (whole blocks)."""
+    bt = wl.block_table
+    n = 0
+    while n < bt.shape[1] and np.all(bt[:, n] == bt[0, n]) and \
+            (n + 1) * 16 <= int(wl.context_lens.min()):
+        n += 1
+    return n * 16
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp16", "int8"])
+def test_small_prefix_workload_vs_oracle(pa, kv_dtype):
+    wl = gen.make("prefix_shared", small=True, overrides=dict(kv_dtype=kv_dtype))
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    pre = prefix_len_of(wl)
+    say(f"shared prefix {kv_dtype}: prefix={pre} lens={wl.context_lens.tolist()}")
+    assert pre == 128
+    d = device_inputs(wl, vals)
+    out, lse = run_prefix(pa, wl, d, pre)
+    want, want_lse = oracle_decode(wl, vals)
+    check_close(out.cpu().numpy(), want, f"shared prefix {kv_dtype}")
+    np.testing.assert_allclose(lse.cpu().numpy(), want_lse, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("G,D,int8", [(1, 64, False), (2, 128, True), (4, 128, False),
+                                      (8, 64, True), (16, 128, False)])
+def test_query_tiles_and_groups(pa, G, D, int8):
+    """Query tiles of 16 cut across sequences and heads (batch * G not a
+    multiple of 16), every supported group size; prefix of 3 blocks."""
+    over = dict(batch=7, q_heads=G * 2, kv_heads=2, head_dim=D, prefix=48, smin=1, smax=300,
+                kv_dtype="int8" if int8 else "fp16")
+    wl = gen.make("prefix_shared", seed=40 + G + D + int8, small=True, overrides=over)
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    pre = prefix_len_of(wl)
+    assert pre == 48
+    d = device_inputs(wl, vals)
+    say(f"tiles G={G} D={D} int8={int8} lens={wl.context_lens.tolist()}")
+    out = run_prefix(pa, wl, d, pre, return_lse=False)
+    want, _ = oracle_decode(wl, vals)
+    check_close(out.cpu().numpy(), want, f"tiles G={G} D={D} int8={int8}")
+
+
+def test_prefix_shorter_than_shared_part_and_empty_suffixes(pa):
+    """prefix_len below the shared length (the rest counts as suffix), a
+    sequence that is exactly the prefix (empty suffix), one-block prefix."""
+    wl = gen.make("prefix_shared", small=True, seed=55)
+    wl.context_lens[2] = 128                  # exactly the shared blocks
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    d = device_inputs(wl, vals)
+    d["context_lens"] = t(wl.context_lens)
+    want, want_lse = oracle_decode(wl, vals)
+    for pre in (16, 64, 128):
+        out, lse = run_prefix(pa, wl, d, pre)
+        check_close(out.cpu().numpy(), want, f"prefix_len={pre}")
+        np.testing.assert_allclose(lse.cpu().numpy(), want_lse, rtol=0, atol=1e-4)
+
+
+def test_sequence_shorter_than_prefix_gets_nan_rows(pa):
+    wl = gen.make("prefix_shared", small=True, seed=56)
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    lens = wl.context_lens.copy()
+    lens[1] = 100                            # below prefix_len = 128: contract broken
+    d = device_inputs(wl, vals)
+    d["context_lens"] = t(lens)
+    out = run_prefix(pa, wl, d, 128, return_lse=False).cpu().numpy()
+    assert np.isnan(out[1].astype(np.float32)).all()
+    want, _ = oracle_decode(wl, vals)
+    keep = [b for b in range(wl.batch) if b != 1]
+    check_close(out[keep], want[keep], "rows beside the broken one")
+
+
+def test_matches_plain_decode(pa):
+    """Same inputs through pa_decode and the shared-prefix path."""
+    wl = gen.make("prefix_shared", small=True, seed=57)
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    d = device_inputs(wl, vals)
+    a = run_prefix(pa, wl, d, 128, return_lse=False).float()
+    b = pa.decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"],
+                  scale=wl.scale, max_context_len=wl.max_context_len).float()
+    err = (a - b).abs().max().item()
+    say(f"shared prefix vs pa_decode: max_abs={err:.3e}")
+    assert err <= 2e-3
+
+
+def test_full_size_prefix_workload_sampled_rows(pa):
+    """The 64-sequence, 1024-token-prefix workload at full size (poisoned
+    unused blocks and tail slots), sampled rows against the oracle."""
+    wl = gen.make("prefix_shared", poison=True)
+    say(f"full prefix_shared: B={wl.batch} NB={wl.num_blocks} max_ctx={wl.max_context_len}")
+    vals = gen.fill_torch(wl, DEV)
+    d = dict(vals)
+    d["block_table"] = t(wl.block_table)
+    d["context_lens"] = t(wl.context_lens)
+    out, lse = run_prefix(pa, wl, d, 1024)
+    out = out.cpu().numpy()
+    assert np.isfinite(out).all() and np.isfinite(lse.cpu().numpy()).all()
+    rng = np.random.default_rng(wl.seed)
+    rows = [(int(rng.integers(wl.batch)), int(rng.integers(wl.q_heads))) for _ in range(6)]
+    rows += [(0, 0), (wl.batch - 1, wl.q_heads - 1)]
+    host = _host_copy(wl, d)
+    want, _ = oracle_decode(wl, host, rows=rows)
+    got = np.stack([out[b, h] for b, h in rows])
+    check_close(got, np.stack([want[b, h] for b, h in rows]), "prefix_shared sampled rows")
