@@ -14,18 +14,16 @@
 // keeps span 1.  When batch * kv_heads alone reaches the target, span is 1
 // (the library then normally picks one partition per sequence instead).
 //
-// Items are (run, head group) pairs over the real runs only, in the order
-// (run index, sequence, head group): first run 0 of every sequence, then
-// run 1 of every sequence that has one, and so on; workgroup i takes item
-// i.  Run index k is held by the c_k sequences with more than k runs, so
-// cum(k) = sum_b min(runs_b, k) runs precede level k.  With uniform lengths
-// this is simply run-index-major order; consecutive workgroups, dealt
-// round-robin to the eight XCDs, are different sequences and head groups of
-// the same run index.  (Measured on MI355X, this order streams faster than
-// sequence-major or per-XCD contiguous orders of the same runs.)  There are
-// at most target_waves / wpg items of wpg-head workgroups when batch *
-// kv_heads is below the target; the host launches that many workgroups and
-// those left without an item exit.
+// Items are (run, head group) pairs over the real runs only, numbered
+// sequence by sequence: sequence b owns runs [R_b, R_b + runs_b), R_b the
+// prefix sum of runs over the sequences before it, and head groups are
+// fastest.  Workgroup i takes item i; consecutive workgroups are dealt
+// round-robin to the eight XCDs.  (Measured on MI355X: as fast as numbering
+// by run index first on uniform lengths and 3 % faster on mixed lengths;
+// dealing each XCD a contiguous share of the items was 6-19 % slower.)
+// There are at most target_waves / wpg items of wpg-head workgroups when
+// batch * kv_heads is below the target; the host launches that many
+// workgroups and those left without an item exit.
 #pragma once
 
 #include "pa_internal.h"
@@ -42,12 +40,6 @@ struct RunSlot {
 __device__ inline int wave_sum(int x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return __builtin_amdgcn_readfirstlane(x);
-}
-
-__device__ inline int wave_max(int x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off));
   return __builtin_amdgcn_readfirstlane(x);
 }
 
@@ -92,35 +84,29 @@ __device__ inline RunSlot locate_run(const DecodeParams& p, int groups) {
   r.span = span = __builtin_amdgcn_readfirstlane(span);
   auto runs_of = [&](int b0) { return (parts_of(b0) + span - 1) / span; };
 
-  // cum(k): runs at indices below k over the batch
-  auto cum = [&](int k) {
-    long long c = 0;
-    for (int b0 = 0; b0 < p.batch; b0 += 64) c += wave_sum(min(runs_of(b0), k));
-    return c;
-  };
-  int max_r = 0;
-  for (int b0 = 0; b0 < p.batch; b0 += 64) max_r = max(max_r, wave_max(runs_of(b0)));
-  if (item >= cum(max_r)) return r;          // past the last run
-  int lo = 0, hi = max_r - 1;                // largest k with cum(k) <= item
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cum(mid) <= item) lo = mid; else hi = mid - 1;
-  }
-  long long rank = item - cum(lo);           // among the sequences with more than lo runs
+  // the sequence whose runs hold `item`: prefix sum of runs over the lanes
+  int base = 0;                              // runs of the sequences before chunk b0
   for (int b0 = 0; b0 < p.batch; b0 += 64) {
-    const unsigned long long has = __ballot(runs_of(b0) > lo);
-    const int cnt = (int)__builtin_popcountll(has);
-    if (rank < cnt) {
-      const unsigned below = __builtin_amdgcn_mbcnt_hi((unsigned)(has >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo((unsigned)has, 0u));
-      const bool mine = ((has >> lane) & 1ull) && below == (unsigned)rank;
-      r.b = b0 + (int)__builtin_ctzll(__ballot(mine));
-      r.ridx = lo;
+    const int runs = runs_of(b0);
+    int incl = runs;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const int chunk = __builtin_amdgcn_readlane(incl, 63);
+    if (item < base + chunk) {
+      // lanes whose runs all lie before the item form a prefix; the next
+      // lane owns it
+      const int k = (int)__builtin_popcountll(__ballot(base + incl <= item));
+      r.b = b0 + k;
+      r.ridx = item - base - (__builtin_amdgcn_readlane(incl, k) -
+                              __builtin_amdgcn_readlane(runs, k));
       return r;
     }
-    rank -= cnt;
+    base += chunk;
   }
-  return r;                                  // not reached
+  return r;                                  // past the last run: b = -1
 }
 
 }  // namespace pa
