@@ -22,9 +22,25 @@ def logical_to_physical(table_row, token: int):
     return int(table_row[page_index]), offset_in_page
 
 
+def e4m3_brute(code: int) -> float:
+    """Value of an OCP FP8 E4M3 code spelled out with math.ldexp: sign bit,
+    4 exponent bits (bias 7, 0 = subnormal), 3 mantissa bits, all-ones = NaN."""
+    neg = (code >> 7) & 1
+    exp_bits = (code >> 3) & 15
+    man = code & 7
+    if exp_bits == 15 and man == 7:
+        return math.nan
+    if exp_bits == 0:
+        mag = math.ldexp(man, -9)                 # man/8 * 2^-6
+    else:
+        mag = math.ldexp(8 + man, exp_bits - 10)  # (1 + man/8) * 2^(e-7)
+    return -mag if neg else mag
+
+
 def brute_decode(q, k_pool, v_pool, block_table, context_lens, scale,
-                 k_scale=None, v_scale=None):
-    """Nested lists out[b][h][d] and lse[b][h]."""
+                 k_scale=None, v_scale=None, element=float):
+    """Nested lists out[b][h][d] and lse[b][h].  `element` maps a pool
+    element to its value (float for fp16 / int8, e4m3_brute for fp8 codes)."""
     B = len(q)
     Hq = len(q[0])
     D = len(q[0][0])
@@ -43,9 +59,9 @@ def brute_decode(q, k_pool, v_pool, block_table, context_lens, scale,
                 vs = float(v_scale[blk][g][off]) if v_scale is not None else 1.0
                 acc = 0.0
                 for d in range(D):
-                    acc += float(q[b][h][d]) * (float(k_pool[blk][off][g][d]) * ks)
+                    acc += float(q[b][h][d]) * (element(k_pool[blk][off][g][d]) * ks)
                 scores.append(float(scale) * acc)
-                vals.append([float(v_pool[blk][off][g][d]) * vs for d in range(D)])
+                vals.append([element(v_pool[blk][off][g][d]) * vs for d in range(D)])
             if L == 0:
                 ob.append([0.0] * D)
                 lb.append(-math.inf)

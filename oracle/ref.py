@@ -38,13 +38,53 @@ reason in the design notes):
   * the output is indexed [b, h, :] (the page's kernel drops the head index);
   * L = 0 gives a zero output row and lse = -inf;
   * the int8 dequantised value is code * scale evaluated exactly (fp64),
-    not rounded to fp16 as the page's dequantize does.
+    not rounded to fp16 as the page's dequantize does;
+  * FP8, which "二、优化方向" of the discosf.com article names beside INT8
+    without giving a format or scale rule, is the OCP FP8 E4M3 format
+    (largest finite value 448, no infinities); pools hold its raw codes
+    (uint8), dequantised exactly as code value * scale, and the quantiser is
+    the per_channel int8 rule with 448 in place of 127 and rounding to the
+    nearest E4M3 value (ties to the even code), saturating at +-448.
 """
 from __future__ import annotations
 
 import numpy as np
 
 TOKENS_PER_BLOCK = 16
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3_value(code: int) -> float:
+    """Value of one OCP FP8 E4M3 code, from the format's definition (OCP
+    8-bit floating point specification): bit 7 sign, bits 6-3 exponent with
+    bias 7, bits 2-0 mantissa; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111
+    is NaN; there are no infinities, so 0x7E = 1.75 * 2^8 = 448 is the
+    largest finite value."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+FP8_E4M3_VALUES = np.array([fp8_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def fp8_e4m3_to_float(codes) -> np.ndarray:
+    """fp64 values of an array of E4M3 codes (uint8)."""
+    return FP8_E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
+def _element_values(rows: np.ndarray) -> np.ndarray:
+    """fp64 values of pool elements: fp16 or int8 as they are, uint8 as
+    E4M3 codes."""
+    if rows.dtype == np.uint8:
+        return fp8_e4m3_to_float(rows)
+    return rows.astype(np.float64)
 
 
 def blocks_needed(num_tokens: int) -> int:
@@ -60,10 +100,10 @@ def gather_sequence(pool: np.ndarray, table_row: np.ndarray, length: int,
 
     Walks the logical blocks in order and copies each physical block's slots
     (zskr.cn article, PagedAttentionMemory logical-to-physical translation,
-    in token units).  For an int8 pool every code is multiplied by its
-    per-(token, kv head) scale in fp64 (discosf.com article, "三、实现示例",
-    KVCacheQuantizer.dequantize: code times scale broadcast over the last
-    axis)."""
+    in token units).  For an int8 or fp8 pool every code's value is
+    multiplied by its per-(token, kv head) scale in fp64 (discosf.com
+    article, "三、实现示例", KVCacheQuantizer.dequantize: code times scale
+    broadcast over the last axis)."""
     L = int(length)
     D = pool.shape[-1]
     dense = np.empty((L, D), dtype=np.float64)
@@ -72,7 +112,7 @@ def gather_sequence(pool: np.ndarray, table_row: np.ndarray, length: int,
         if not 0 <= phys < pool.shape[0]:
             raise IndexError(f"block id {phys} out of range [0, {pool.shape[0]})")
         n = min(TOKENS_PER_BLOCK, L - j * TOKENS_PER_BLOCK)
-        rows = pool[phys, :n, kv_head, :].astype(np.float64)
+        rows = _element_values(pool[phys, :n, kv_head, :])
         if scale_pool is not None:
             rows = rows * scale_pool[phys, kv_head, :n].astype(np.float64)[:, None]
         dense[j * TOKENS_PER_BLOCK:j * TOKENS_PER_BLOCK + n] = rows
@@ -231,3 +271,41 @@ def ref_quantize_int8(x):
     s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
     codes = np.clip(np.round(x32 / s), -128, 127).astype(np.int8)
     return codes, s[..., 0]
+
+
+def _nearest_e4m3(y) -> np.ndarray:
+    """E4M3 codes of fp32 values: the nearest finite E4M3 value, a tie going
+    to the code with an even mantissa (round half to even), magnitudes at or
+    beyond 448 saturating to 448; the sign bit is the sign of y (so -0.0
+    gives 0x80)."""
+    y = np.asarray(y, dtype=np.float32)
+    pos = FP8_E4M3_VALUES[:0x7F]                   # codes 0 .. 126, increasing
+    a = np.abs(y.astype(np.float64))
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = a - pos[lo]
+    d_hi = pos[hi] - a
+    pick = np.where(d_hi < d_lo, hi, lo)
+    tie = d_hi == d_lo
+    pick = np.where(tie, np.where(hi % 2 == 0, hi, lo), pick)
+    pick = np.where(a >= FP8_E4M3_MAX, 0x7E, pick)
+    return (pick | (np.signbit(y).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def ref_quantize_fp8(x):
+    """Per-(token, kv head) FP8 E4M3 quantisation over the last axis.
+
+    The per_channel rule of KVCacheQuantizer.quantize (discosf.com article,
+    "三、实现示例") with E4M3's largest finite value in place of 127 (the
+    same article's "二、优化方向" names FP8 next to INT8 and gives no rule of
+    its own): in fp32, absmax of |x| over the last axis, scale = absmax /
+    448, a zero scale replaced by 1.0, codes = the E4M3 value nearest to
+    x / scale (ties to even, saturating at +-448).
+    Returns (codes uint8 x.shape, scales fp32 x.shape[:-1])."""
+    x32 = np.asarray(x).astype(np.float32)
+    amax = np.max(np.abs(x32), axis=-1, keepdims=True)
+    s = amax / np.float32(FP8_E4M3_MAX)
+    s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    codes = _nearest_e4m3(x32 / s)
+    return codes, s[..., 0]
+

@@ -308,3 +308,97 @@ def test_pins_catch_planted_mistakes(monkeypatch):
                        ("gather_sequence", one_more), ("attend", no_scale)]:
         assert _brute_pin_fails(monkeypatch, attr, fake), attr
         monkeypatch.undo()
+
+
+# ----------------------------------------------------------------- FP8 E4M3
+
+def test_fp8_code_values_from_format_definition():
+    g = json.load(open(os.path.join(GOLDEN, "fp8_e4m3.json")))
+    for c in g["codes"]:
+        got = ref.fp8_e4m3_value(c["code"])
+        if c["value"] == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == c["value"] and math.copysign(1, got) == math.copysign(1, c["value"])
+
+
+def test_fp8_table_matches_bitwise_spelling_and_is_ordered():
+    for code in range(256):
+        a, b = ref.fp8_e4m3_value(code), brute.e4m3_brute(code)
+        assert (math.isnan(a) and math.isnan(b)) or a == b
+    pos = ref.FP8_E4M3_VALUES[:0x7F]
+    assert np.all(np.diff(pos) > 0)                        # codes 0..126 increase
+    assert np.array_equal(ref.FP8_E4M3_VALUES[0x80:0xFF], -pos)
+    finite = ref.FP8_E4M3_VALUES[np.isfinite(ref.FP8_E4M3_VALUES)]
+    assert len(finite) == 254 and len(np.unique(finite)) == 253   # +-0 share a value
+    assert finite.max() == 448.0
+
+
+def test_fp8_quantiser_worked_rows():
+    g = json.load(open(os.path.join(GOLDEN, "fp8_e4m3.json")))
+    for row in g["rows"]:
+        codes, s = ref.ref_quantize_fp8(np.array([row["x"]], dtype=np.float32))
+        assert s[0] == np.float32(row["scale"])
+        assert codes[0].tolist() == row["codes"]
+
+
+def _brute_nearest_code(y: float) -> int:
+    """Scan every finite E4M3 code for the nearest value; ties to the even
+    code; beyond 448 saturate."""
+    mag = abs(y)
+    best, best_d = None, None
+    for c in range(0x7F):
+        d = abs(brute.e4m3_brute(c) - mag)
+        if best is None or d < best_d or (d == best_d and c % 2 == 0):
+            best, best_d = c, d
+    if mag >= 448.0:
+        best = 0x7E
+    return best | (0x80 if math.copysign(1.0, y) < 0 else 0)
+
+
+def test_fp8_quantiser_properties_and_brute_rounding():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((48, 2, 32), dtype=np.float32).astype(np.float16)
+    x[3, 1] = 0
+    codes, s = ref.ref_quantize_fp8(x)
+    assert codes.dtype == np.uint8 and s.dtype == np.float32 and s.shape == (48, 2)
+    assert s[3, 1] == 1.0 and not codes[3, 1].any()
+    vals = ref.fp8_e4m3_to_float(codes)
+    assert np.all(np.isfinite(vals)) and np.abs(vals).max() <= 448.0
+    nz = np.abs(x.astype(np.float32)).max(-1) > 0
+    assert np.all(np.abs(vals).max(-1)[nz] == 448.0)       # the absmax element maps to 448
+    # error: half the E4M3 spacing at the value (2^-3 relative, 2^-10 absolute
+    # in the subnormal range), plus the fp32 rounding of x / s
+    y = x.astype(np.float64) / s[..., None]
+    half_gap = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(np.abs(y - vals) <= half_gap * (1 + 1e-6) + np.abs(y) * 2.0 ** -23)
+    for i in range(0, 48, 5):
+        for j in range(32):
+            q = float(np.float32(x[i, 0, j]) / np.float32(s[i, 0]))
+            assert codes[i, 0, j] == _brute_nearest_code(q)
+    # every tie between neighbouring codes, both signs
+    pos = ref.FP8_E4M3_VALUES[:0x7F]
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    for sign in (1.0, -1.0):
+        got = ref._nearest_e4m3(sign * mids)
+        want = [_brute_nearest_code(sign * float(m)) for m in mids]
+        assert got.tolist() == want
+    assert ref._nearest_e4m3(np.float32([500.0, -1e30]))[0] == 0x7E
+
+
+def test_fp8_decode_against_brute_force():
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, D, NB = 2, 4, 2, 8, 6
+    q = rng.standard_normal((B, Hq, D), dtype=np.float32).astype(np.float16)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    kp = rng.choice(finite, size=(NB, 16, Hkv, D))
+    vp = rng.choice(finite, size=(NB, 16, Hkv, D))
+    ks = rng.uniform(1e-3, 2e-2, size=(NB, Hkv, 16)).astype(np.float32)
+    vs = rng.uniform(1e-3, 2e-2, size=(NB, Hkv, 16)).astype(np.float32)
+    bt = np.array([[4, 1, 0], [2, 5, 3]], dtype=np.int32)
+    cl = np.array([37, 20], dtype=np.int32)
+    out, lse = ref.ref_decode(q, kp, vp, bt, cl, 0.3, ks, vs)
+    bo, bl = brute.brute_decode(q.tolist(), kp.tolist(), vp.tolist(), bt.tolist(), cl.tolist(),
+                                0.3, ks.tolist(), vs.tolist(), element=brute.e4m3_brute)
+    np.testing.assert_allclose(out, np.array(bo), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(bl), rtol=1e-12, atol=1e-12)
