@@ -4,7 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step = one pass of the hot path over one batch: the KV write of each
-sequence's new token into its slot (fp16 copy, or quantising int8 write),
+sequence's new token into its slot (fp16 copy, or quantising int8 / FP8 write),
 then paged decode attention over every sequence's context (split-K partition
 kernel, plus the log-sum-exp merge when the context spans several
 partitions).  Inputs are seeded synthetic tensors already resident in HBM.
@@ -42,7 +42,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "paged-attn decode: achieved KV HBM GB/s (% of peak) and sequences/s per layer"
 HEADLINE = "llama2_7b"
-OTHERS = ["gqa70b_mixed", "prefix_shared", "long128k_int8", "tiny_gqa"]
+OTHERS = ["gqa70b_mixed", "prefix_shared", "long128k_int8", "long128k_fp8", "tiny_gqa"]
 
 
 def parse():
@@ -119,15 +119,16 @@ class Case:
                                                    shared_prefix)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         self.out = torch.empty_like(vals["q"])
-        self.int8 = wl.kv_dtype == "int8"
+        self.q8 = wl.kv_dtype in ("int8", "fp8")             # 8-bit codes + scales
         self.kv_bytes = gen.kv_ideal_bytes(wl)                # unique bytes
         self.kv_bytes_logical = gen.kv_ideal_bytes(wl, unique=False)
 
     def write(self):
         v = self.v
-        if self.int8:
-            self.pa.write_kv_int8(v["k_new"], v["v_new"], self.slots, v["k_pool"], v["v_pool"],
-                                  v["k_scale"], v["v_scale"])
+        if self.q8:
+            fn = self.pa.write_kv_int8 if self.wl.kv_dtype == "int8" else self.pa.write_kv_fp8
+            fn(v["k_new"], v["v_new"], self.slots, v["k_pool"], v["v_pool"], v["k_scale"],
+               v["v_scale"])
         else:
             self.pa.write_kv(v["k_new"], v["v_new"], self.slots, v["k_pool"], v["v_pool"])
 
@@ -143,11 +144,11 @@ class Case:
                                          workspace=self.ws, k_scale=v.get("k_scale"),
                                          v_scale=v.get("v_scale"))
         elif self.n_part == 1:
-            if self.int8:
-                self.pa.decode_int8(v["q"], v["k_pool"], v["v_pool"], v["k_scale"], v["v_scale"],
-                                    self.bt, self.cl, scale=wl.scale, partition_size=self.P,
-                                    max_context_len=wl.max_context_len, out=self.out,
-                                    workspace=self.ws)
+            if self.q8:
+                fn = self.pa.decode_int8 if wl.kv_dtype == "int8" else self.pa.decode_fp8
+                fn(v["q"], v["k_pool"], v["v_pool"], v["k_scale"], v["v_scale"], self.bt, self.cl,
+                   scale=wl.scale, partition_size=self.P, max_context_len=wl.max_context_len,
+                   out=self.out, workspace=self.ws)
             else:
                 self.pa.decode(v["q"], v["k_pool"], v["v_pool"], self.bt, self.cl, scale=wl.scale,
                                partition_size=self.P, max_context_len=wl.max_context_len,
@@ -335,8 +336,8 @@ def cpu_baseline(case, budget_s):
     wl = case.wl
     v = case.v
     host = {k: v[k].cpu().numpy() for k in ("q", "k_pool", "v_pool")}
-    ks = v["k_scale"].cpu().numpy() if case.int8 else None
-    vs = v["v_scale"].cpu().numpy() if case.int8 else None
+    ks = v["k_scale"].cpu().numpy() if case.q8 else None
+    vs = v["v_scale"].cpu().numpy() if case.q8 else None
     done_bytes, done_seqs = 0, 0
     per_tok = case.kv_bytes_logical / max(1, int(wl.context_lens.sum()))
     with threadpool_limits(limits=1):

@@ -116,6 +116,28 @@ int pa_write_kv_int8(const void* k_new, const void* v_new, const int32_t* slot_m
                      int head_dim, void* stream);
 
 /*
+ * FP8 KV cache.  The discosf.com article "KV Cache 优化与显存管理" (section
+ * "二、优化方向") names FP8 beside INT8 as a KV-cache precision that halves
+ * its memory, without a format or a scale rule.  This library's FP8 is the
+ * OCP FP8 E4M3 format (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; largest finite value 448; S.1111.111 is NaN), which gfx950 converts
+ * natively.  Pools hold raw codes, uint8 [num_blocks, block_size, kv_heads,
+ * head_dim]; scales are fp32 [num_blocks, kv_heads, block_size] as for int8,
+ * and an element's value is E4M3(code) * scale.
+ *
+ * pa_write_kv_fp8: the quantising write, per (token, kv head) row, by the
+ * per_channel rule of the int8 write with 448 in place of 127: scale =
+ * absmax / 448 in fp32 (IEEE division; zero -> 1.0), code = the E4M3 value
+ * nearest to x / scale (fp32 IEEE division), ties to the even code,
+ * magnitudes at or above 448 saturating to 448.  Arguments, skip rules and
+ * status codes as for pa_write_kv_int8.
+ */
+int pa_write_kv_fp8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                    uint8_t* k_pool, uint8_t* v_pool, float* k_scale, float* v_scale,
+                    int num_tokens, int num_blocks, int block_size, int kv_heads,
+                    int head_dim, void* stream);
+
+/*
  * Partition size the library uses for these shapes when partition_size is
  * 0, else partition_size itself (a multiple of 16).  The library's choice:
  * 256 tokens, the finest split, with runs of partitions merged on the
@@ -175,13 +197,26 @@ int pa_decode_int8(void* out, float* lse_out, const void* q, const int8_t* k_poo
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode over an FP8 (OCP E4M3) cache with fp32 per-(token, kv head)
+ * scales (see pa_write_kv_fp8): codes become exact fp16 values on the way
+ * in; the scales enter as for pa_decode_int8.
+ */
+int pa_decode_fp8(void* out, float* lse_out, const void* q, const uint8_t* k_pool,
+                  const uint8_t* v_pool, const float* k_scale, const float* v_scale,
+                  const int32_t* block_table, int max_blocks, const int32_t* context_lens,
+                  int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
+                  int block_size, int num_blocks, float scale, int partition_size,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The two stages pa_decode runs, exported for callers that combine
  * partial results from several sources (for example one sequence's
  * context split across devices, or a shared prefix attended once and
  * merged with each private suffix).
  *
- * pa_decode_partials / pa_decode_partials_int8: same arguments as
- * pa_decode / pa_decode_int8 without out and lse_out; always write the
+ * pa_decode_partials / pa_decode_partials_int8 / pa_decode_partials_fp8:
+ * same arguments as pa_decode / pa_decode_int8 / pa_decode_fp8 without out
+ * and lse_out; always write the
  * partition records into the workspace, which must hold
  * pa_decode_workspace_size(..., partition_size resolved, ...) bytes
  * computed with max_context_len > partition_size, i.e. room for
@@ -226,6 +261,14 @@ int pa_decode_partials_int8(const void* q, const int8_t* k_pool, const int8_t* v
                             int num_blocks, float scale, int partition_size,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+int pa_decode_partials_fp8(const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, int max_blocks,
+                           const int32_t* context_lens, int max_context_len, int batch,
+                           int q_heads, int kv_heads, int head_dim, int block_size,
+                           int num_blocks, float scale, int partition_size,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,
                       int max_context_len, int batch, int q_heads, int head_dim,
                       int partition_size, const void* workspace, size_t workspace_bytes,
@@ -257,8 +300,8 @@ int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,
  *                    gets NaN rows.
  *   workspace        pa_decode_shared_prefix_workspace_size(...) bytes,
  *                    required (the split always runs).
- *   all other arguments as for pa_decode / pa_decode_int8; the suffixes use
- *   the library's 256-token partitions.
+ *   all other arguments as for pa_decode / pa_decode_int8 / pa_decode_fp8;
+ *   the suffixes use the library's 256-token partitions.
  *
  * Returns PA_ERR_SHAPE for a bad prefix_len, otherwise the codes of
  * pa_decode.  Launches, in order on `stream`: the suffix partition kernel,
@@ -283,6 +326,15 @@ int pa_decode_shared_prefix_int8(void* out, float* lse_out, const void* q, const
                                  int head_dim, int block_size, int num_blocks, float scale,
                                  int prefix_len, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+int pa_decode_shared_prefix_fp8(void* out, float* lse_out, const void* q, const uint8_t* k_pool,
+                                const uint8_t* v_pool, const float* k_scale,
+                                const float* v_scale, const int32_t* block_table,
+                                int max_blocks, const int32_t* context_lens,
+                                int max_context_len, int batch, int q_heads, int kv_heads,
+                                int head_dim, int block_size, int num_blocks, float scale,
+                                int prefix_len, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 #ifdef __cplusplus
 }

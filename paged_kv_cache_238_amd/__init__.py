@@ -9,8 +9,13 @@ package raises.
 Functions mirror the C entry points:
   write_kv(k_new, v_new, slot_mapping, k_pool, v_pool)
   write_kv_int8(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale)
+  write_kv_fp8(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale)
   decode(q, k_pool, v_pool, block_table, context_lens, ...)
   decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, ...)
+  decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, ...)
+
+FP8 pools hold raw OCP E4M3 codes: torch.uint8 tensors (a torch.float8_e4m3fn
+tensor is accepted and viewed as its bytes).
   decode_partials(...), decode_partials_int8(...), merge_partials(...)
   decode_shared_prefix(q, k_pool, v_pool, block_table, context_lens, prefix_len, ...)
   workspace_size(...), partition_size(...), shared_prefix_workspace_size(...)
@@ -23,7 +28,8 @@ import os
 
 __all__ = [
     "PaError", "LIB_PATH", "lib", "status_string", "write_kv", "write_kv_int8",
-    "partition_size", "workspace_size", "decode", "decode_int8", "decode_partials",
+    "write_kv_fp8", "partition_size", "workspace_size", "decode", "decode_int8",
+    "decode_fp8", "decode_partials",
     "decode_partials_int8", "merge_partials", "decode_shared_prefix",
     "shared_prefix_workspace_size", "EXPORTS",
 ]
@@ -54,22 +60,29 @@ EXPORTS = {
     "pa_status_string": (ctypes.c_char_p, [_i]),
     "pa_write_kv": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "pa_write_kv_int8": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
+    "pa_write_kv_fp8": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "pa_decode_partition_size": (_i, [_i, _i, _i, _i, _i, _i]),
     "pa_decode_workspace_size": (_z, [_i, _i, _i, _i, _i, _i]),
     "pa_decode": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i,
                        _p, _z, _p]),
     "pa_decode_int8": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
                             _i, _f, _i, _p, _z, _p]),
+    "pa_decode_fp8": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
+                           _i, _f, _i, _p, _z, _p]),
     "pa_decode_partials": (_i, [_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i,
                                 _p, _z, _p]),
     "pa_decode_partials_int8": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
                                      _i, _f, _i, _p, _z, _p]),
+    "pa_decode_partials_fp8": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
+                                    _i, _f, _i, _p, _z, _p]),
     "pa_merge_partials": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _z, _p]),
     "pa_decode_shared_prefix_workspace_size": (_z, [_i, _i, _i, _i, _i, _i]),
     "pa_decode_shared_prefix": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
                                      _i, _f, _i, _p, _z, _p]),
     "pa_decode_shared_prefix_int8": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i,
                                           _i, _i, _i, _i, _f, _i, _p, _z, _p]),
+    "pa_decode_shared_prefix_fp8": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i,
+                                         _i, _i, _i, _i, _f, _i, _p, _z, _p]),
 }
 for _name, (_res, _args) in EXPORTS.items():
     _fn = getattr(lib, _name)
@@ -145,13 +158,21 @@ def write_kv(k_new, v_new, slot_mapping, k_pool, v_pool) -> None:
                            _ptr(v_pool), T, NB, bs, Hkv, D, _stream(k_pool)), "pa_write_kv")
 
 
-def write_kv_int8(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale) -> None:
-    """Quantise token i's K/V rows per (token, kv head) into the int8 pools
-    and their fp32 scales at slot slot_mapping[i]."""
+def _codes(t):
+    """An FP8 pool as its uint8 codes (float8_e4m3fn tensors are viewed)."""
     torch = _torch()
-    _need(k_pool, "k_pool", torch.int8, 4)
+    fp8 = getattr(torch, "float8_e4m3fn", None)
+    if fp8 is not None and isinstance(t, torch.Tensor) and t.dtype == fp8:
+        return t.view(torch.uint8)
+    return t
+
+
+def _write_q8(fn, name, pool_dtype, k_new, v_new, slot_mapping, k_pool, v_pool, k_scale,
+              v_scale):
+    torch = _torch()
+    _need(k_pool, "k_pool", pool_dtype, 4)
     dev = k_pool.device
-    _need(v_pool, "v_pool", torch.int8, 4, dev)
+    _need(v_pool, "v_pool", pool_dtype, 4, dev)
     _need(k_scale, "k_scale", torch.float32, 3, dev)
     _need(v_scale, "v_scale", torch.float32, 3, dev)
     _need(k_new, "k_new", torch.float16, 3, dev)
@@ -162,10 +183,23 @@ def write_kv_int8(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale) 
     if v_pool.shape != k_pool.shape or k_scale.shape != (NB, Hkv, bs) \
             or v_scale.shape != k_scale.shape or k_new.shape != (T, Hkv, D) \
             or v_new.shape != k_new.shape or slot_mapping.shape[0] != T:
-        raise ValueError("write_kv_int8: inconsistent shapes")
-    _check(lib.pa_write_kv_int8(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_pool),
-                                _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), T, NB, bs, Hkv, D,
-                                _stream(k_pool)), "pa_write_kv_int8")
+        raise ValueError(f"{name}: inconsistent shapes")
+    _check(fn(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_pool), _ptr(v_pool),
+              _ptr(k_scale), _ptr(v_scale), T, NB, bs, Hkv, D, _stream(k_pool)), name)
+
+
+def write_kv_int8(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale) -> None:
+    """Quantise token i's K/V rows per (token, kv head) into the int8 pools
+    and their fp32 scales at slot slot_mapping[i]."""
+    _write_q8(lib.pa_write_kv_int8, "pa_write_kv_int8", _torch().int8, k_new, v_new,
+              slot_mapping, k_pool, v_pool, k_scale, v_scale)
+
+
+def write_kv_fp8(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale) -> None:
+    """Quantise token i's K/V rows per (token, kv head) to FP8 E4M3 codes in
+    the uint8 pools, with their fp32 scales, at slot slot_mapping[i]."""
+    _write_q8(lib.pa_write_kv_fp8, "pa_write_kv_fp8", _torch().uint8, k_new, v_new,
+              slot_mapping, _codes(k_pool), _codes(v_pool), k_scale, v_scale)
 
 
 def partition_size(batch, q_heads, kv_heads, head_dim, max_context_len, partition_size=0) -> int:
@@ -263,23 +297,45 @@ def decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, 
     return (out, lse) if return_lse else out
 
 
+def decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, scale=None,
+               partition_size=0, max_context_len=None, out=None, return_lse=False,
+               workspace=None):
+    """Paged decode over an FP8 (E4M3 codes, uint8) cache with fp32
+    per-(token, kv head) scales."""
+    torch = _torch()
+    k_pool, v_pool = _codes(k_pool), _codes(v_pool)
+    B, Hq, Hkv, D, NB, bs, MB, L = _decode_args(q, k_pool, v_pool, block_table, context_lens,
+                                                torch.uint8, max_context_len, k_scale, v_scale)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out, lse = _alloc_out(q, out, return_lse)
+    ws = _workspace(q, B, Hq, Hkv, D, L, partition_size, workspace)
+    _check(lib.pa_decode_fp8(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                             _ptr(k_scale), _ptr(v_scale), _ptr(block_table), MB,
+                             _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB, scale,
+                             partition_size, _ptr(ws), ws.numel(), _stream(q)),
+           "pa_decode_fp8")
+    return (out, lse) if return_lse else out
+
+
 def decode_partials(q, k_pool, v_pool, block_table, context_lens, workspace, scale=None,
                     partition_size=0, max_context_len=None, k_scale=None, v_scale=None):
     """Stage 1 of decode: write the per-partition records into `workspace`
     (uint8 device tensor of >= workspace_size(...) bytes).  Returns the
     resolved partition size."""
     torch = _torch()
-    int8 = k_pool.dtype == torch.int8
+    k_pool, v_pool = _codes(k_pool), _codes(v_pool)
+    q8 = k_pool.dtype in (torch.int8, torch.uint8)
     B, Hq, Hkv, D, NB, bs, MB, L = _decode_args(
-        q, k_pool, v_pool, block_table, context_lens, torch.int8 if int8 else torch.float16,
-        max_context_len, k_scale if int8 else None, v_scale if int8 else None)
+        q, k_pool, v_pool, block_table, context_lens, k_pool.dtype if q8 else torch.float16,
+        max_context_len, k_scale if q8 else None, v_scale if q8 else None)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     nbytes = workspace.numel() * workspace.element_size()
-    if int8:
-        st = lib.pa_decode_partials_int8(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
-                                         _ptr(v_scale), _ptr(block_table), MB, _ptr(context_lens),
-                                         L, B, Hq, Hkv, D, bs, NB, scale, partition_size,
-                                         _ptr(workspace), nbytes, _stream(q))
+    if q8:
+        fn = lib.pa_decode_partials_int8 if k_pool.dtype == torch.int8 \
+            else lib.pa_decode_partials_fp8
+        st = fn(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                _ptr(block_table), MB, _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB, scale,
+                partition_size, _ptr(workspace), nbytes, _stream(q))
     else:
         st = lib.pa_decode_partials(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), MB,
                                     _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB, scale,
@@ -316,24 +372,30 @@ def decode_shared_prefix(q, k_pool, v_pool, block_table, context_lens, prefix_le
                          k_scale=None, v_scale=None):
     """Decode where every sequence's first `prefix_len` tokens sit in the same
     blocks (row 0's ids); the shared blocks are read once per kv head for all
-    sequences.  int8 pools when k_scale / v_scale are given."""
+    sequences.  int8 or fp8 (uint8 codes) pools when k_scale / v_scale are
+    given."""
     torch = _torch()
-    int8 = k_scale is not None
+    k_pool, v_pool = _codes(k_pool), _codes(v_pool)
+    q8 = k_scale is not None
     B, Hq, Hkv, D, NB, bs, MB, L = _decode_args(
-        q, k_pool, v_pool, block_table, context_lens, torch.int8 if int8 else torch.float16,
+        q, k_pool, v_pool, block_table, context_lens, k_pool.dtype if q8 else torch.float16,
         max_context_len, k_scale, v_scale)
+    if q8 and k_pool.dtype not in (torch.int8, torch.uint8):
+        raise ValueError("decode_shared_prefix: scaled pools must be int8 or uint8 (fp8) codes")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     out, lse = _alloc_out(q, out, return_lse)
     need = shared_prefix_workspace_size(B, Hq, Hkv, D, L, int(prefix_len))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     nbytes = workspace.numel() * workspace.element_size()
-    if int8:
-        _check(lib.pa_decode_shared_prefix_int8(
+    if q8:
+        fn = lib.pa_decode_shared_prefix_int8 if k_pool.dtype == torch.int8 \
+            else lib.pa_decode_shared_prefix_fp8
+        _check(fn(
             _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
             _ptr(v_scale), _ptr(block_table), MB, _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB,
             scale, int(prefix_len), _ptr(workspace), nbytes, _stream(q)),
-            "pa_decode_shared_prefix_int8")
+            "pa_decode_shared_prefix (8-bit)")
     else:
         _check(lib.pa_decode_shared_prefix(
             _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), MB,

@@ -104,15 +104,33 @@ __device__ __forceinline__ void to_f32(const uint4& c, float (&f)[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] = (float)v[e];
 }
-__device__ __forceinline__ void to_f32(const uint2& c, float (&f)[8]) {
+__device__ __forceinline__ void i8_to_f32(const uint2& c, float (&f)[8]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) f[e] = (float)(int)(int8_t)(c.x >> (8 * e));
 #pragma unroll
   for (int e = 0; e < 4; ++e) f[4 + e] = (float)(int)(int8_t)(c.y >> (8 * e));
 }
+// Eight OCP E4M3 codes, exact (v_cvt_pk_f32_fp8, two codes per call).
+__device__ __forceinline__ void f8_to_f32(const uint2& c, float (&f)[8]) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
+  const auto e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+  f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+  f[4] = d[0]; f[5] = d[1]; f[6] = e[0]; f[7] = e[1];
+}
+// Values of one chunk of K/V elements in format KV.
+template <int KV>
+__device__ __forceinline__ void kv_to_f32(const typename KvChunk<KV != kKvF16>::T& c,
+                                          float (&f)[8]) {
+  if constexpr (KV == kKvI8) i8_to_f32(c, f);
+  else if constexpr (KV == kKvF8) f8_to_f32(c, f);
+  else to_f32(c, f);
+}
 
-template <int D, int G, bool I8>
+template <int D, int G, int KV>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParams p) {
+  constexpr bool I8 = KV != kKvF16;          // 8-bit codes with per-token scales
   constexpr int LPR = D / 8;                 // lanes per token row
   constexpr int RPW = 64 / LPR;              // token rows per wave load
   constexpr int NL = kBlockTokens / RPW;     // wave loads per block
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float kf[I8 ? 8 : 1];
-      if constexpr (I8) to_f32(R.k[i], kf);
+      if constexpr (I8) kv_to_f32<KV>(R.k[i], kf);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float part_dot = 0.f;
@@ -294,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     float vsc[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      to_f32(R.v[i], vf[i]);
+      kv_to_f32<KV>(R.v[i], vf[i]);
       vsc[i] = R.vs[i];
       if constexpr (TAIL) {
         if (r + RPW * i >= valid) {   // masked row: value and its scale may be NaN
@@ -429,35 +447,45 @@ int waves_per_group(const DecodeParams& p) {
   return (p.kv_heads % 4 == 0) ? 4 : (p.kv_heads % 2 == 0) ? 2 : 1;
 }
 
-template <int D, int G, bool I8>
+template <int D, int G, int KV>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   const int wpg = waves_per_group(p);
   const unsigned grid = decode_workgroups(p, wpg);
-  hipLaunchKernelGGL((decode_valu_kernel<D, G, I8>), dim3(grid), dim3(64 * wpg), 0, stream, p);
+  hipLaunchKernelGGL((decode_valu_kernel<D, G, KV>), dim3(grid), dim3(64 * wpg), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool I8>
+template <int D, int KV>
 hipError_t dispatch_group(const DecodeParams& p, hipStream_t stream) {
   switch (p.q_heads / p.kv_heads) {
-    case 1: return launch_one<D, 1, I8>(p, stream);
-    case 2: return launch_one<D, 2, I8>(p, stream);
+    case 1: return launch_one<D, 1, KV>(p, stream);
+    case 2: return launch_one<D, 2, KV>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t dispatch_format(const DecodeParams& p, int kv, hipStream_t stream) {
+  switch (kv) {
+    case kKvF16: return dispatch_group<D, kKvF16>(p, stream);
+    case kKvI8: return dispatch_group<D, kKvI8>(p, stream);
+    case kKvF8: return dispatch_group<D, kKvF8>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_valu(const DecodeParams& p, bool int8, hipStream_t stream) {
-  if (p.head_dim == 128) return int8 ? dispatch_group<128, true>(p, stream) : dispatch_group<128, false>(p, stream);
-  if (p.head_dim == 64) return int8 ? dispatch_group<64, true>(p, stream) : dispatch_group<64, false>(p, stream);
+hipError_t launch_decode_valu(const DecodeParams& p, int kv, hipStream_t stream) {
+  if (p.head_dim == 128) return dispatch_format<128>(p, kv, stream);
+  if (p.head_dim == 64) return dispatch_format<64>(p, kv, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeParams& p, bool int8, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int kv, hipStream_t stream) {
   const int group = p.q_heads / p.kv_heads;
-  if (group >= 4) return launch_decode_mfma(p, int8, stream);
-  return launch_decode_valu(p, int8, stream);
+  if (group >= 4) return launch_decode_mfma(p, kv, stream);
+  return launch_decode_valu(p, kv, stream);
 }
 
 }  // namespace pa

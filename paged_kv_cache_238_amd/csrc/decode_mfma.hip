@@ -18,7 +18,9 @@
 //
 // int8 caches: codes are converted exactly to fp16 (0x6400 | (x ^ 0x80) is
 // 1152 + x; subtracting 1152 in packed fp16 leaves x), the per-token K scale
-// is applied to the score and the V scale to the probability.
+// is applied to the score and the V scale to the probability.  FP8 (OCP
+// E4M3) caches: every E4M3 value is exact in fp16, two codes per
+// v_cvt_scalef32_pk_f16_fp8 (scale 1); the scales are applied as for int8.
 //
 // Method and readings are those of the VALU kernel (zskr.cn ATB
 // PagedAttention article, section "PagedAttention 的 Attention 计算修改",
@@ -115,6 +117,19 @@ __device__ __forceinline__ void i8x16_to_h16(const uint4& c, uint4& first, uint4
   i8x4_to_h4(c.w, second.z, second.w);
 }
 
+// Four E4M3 codes -> four fp16 (codes 0, 1 in lo; 2, 3 in hi).
+__device__ __forceinline__ void f8x4_to_h4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, true));
+}
+
+__device__ __forceinline__ void f8x16_to_h16(const uint4& c, uint4& first, uint4& second) {
+  f8x4_to_h4(c.x, first.x, first.y);
+  f8x4_to_h4(c.y, first.z, first.w);
+  f8x4_to_h4(c.z, second.x, second.y);
+  f8x4_to_h4(c.w, second.z, second.w);
+}
+
 template <int D, bool I8>
 struct Geometry {
   // 16-byte global loads per lane per block for K (and again for V).
@@ -143,9 +158,10 @@ struct Geometry {
 // whole partition and writes its own record.  The waves of a workgroup thus
 // read neighbouring slices of the same token rows at the same time, and a
 // wave's start-up (length, block ids, Q) is paid once per partition.
-template <int D, int G, bool I8, bool PREFIX>
+template <int D, int G, int KV, bool PREFIX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES_PER_EU)))
 void decode_mfma_kernel(const DecodeParams p) {
+  constexpr bool I8 = KV != kKvF16;          // 8-bit codes with per-token scales
   using Geo = Geometry<D, I8>;
   constexpr int NLD = Geo::kLoads;
   constexpr int NKK = Geo::kSteps;
@@ -257,7 +273,7 @@ void decode_mfma_kernel(const DecodeParams p) {
 
   // int8: sum over head_dim of q for head li (removes the 1152 bias of K).
   float qbias = 0.f;
-  if constexpr (I8) {
+  if constexpr (KV == kKvI8) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
@@ -326,7 +342,8 @@ void decode_mfma_kernel(const DecodeParams p) {
 #pragma unroll
       for (int ld = 0; ld < NLD; ++ld) {
         uint4 a, c;
-        i8x16_to_h16_biased(R.k[ld], a, c);
+        if constexpr (KV == kKvI8) i8x16_to_h16_biased(R.k[ld], a, c);
+        else f8x16_to_h16(R.k[ld], a, c);
         kA[2 * ld] = __builtin_bit_cast(h8, a);
         kA[2 * ld + 1] = __builtin_bit_cast(h8, c);
       }
@@ -347,7 +364,8 @@ void decode_mfma_kernel(const DecodeParams p) {
 #pragma unroll
         for (int ld = 0; ld < NLD; ++ld) {
           uint4 a, c;
-          i8x16_to_h16(R.v[ld], a, c);
+          if constexpr (KV == kKvI8) i8x16_to_h16(R.v[ld], a, c);
+          else f8x16_to_h16(R.v[ld], a, c);
           if (zero_row) a = c = make_uint4(0, 0, 0, 0);
           const int d0 = 64 * ld + 16 * lg;
           *reinterpret_cast<uint4*>(rowp + d0 * 2) = a;
@@ -514,53 +532,71 @@ int waves_per_group(const DecodeParams& p) {
   return (p.kv_heads % 4 == 0) ? 4 : (p.kv_heads % 2 == 0) ? 2 : 1;
 }
 
-template <int D, int G, bool I8>
+template <int D, int G, int KV>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
-  using Geo = Geometry<D, I8>;
+  using Geo = Geometry<D, KV != kKvF16>;
   const int wpg = waves_per_group(p);
   const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes;
   const unsigned grid = decode_workgroups(p, wpg);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, G, I8, false>), dim3(grid), dim3(64 * wpg), lds,
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G, KV, false>), dim3(grid), dim3(64 * wpg), lds,
                      stream, p);
   return hipGetLastError();
 }
 
 // Shared prefix: (query tile, prefix partition, head group) workgroups of up
 // to four kv heads.
-template <int D, bool I8>
+template <int D, int KV>
 hipError_t launch_prefix(const DecodeParams& p, hipStream_t stream) {
-  using Geo = Geometry<D, I8>;
+  using Geo = Geometry<D, KV != kKvF16>;
   const int wpg = (p.kv_heads % 4 == 0) ? 4 : (p.kv_heads % 2 == 0) ? 2 : 1;
   const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes;
   const unsigned grid = (unsigned)((long long)p.prefix_tiles * p.n_part * (p.kv_heads / wpg));
-  hipLaunchKernelGGL((decode_mfma_kernel<D, 16, I8, true>), dim3(grid), dim3(64 * wpg), lds,
+  hipLaunchKernelGGL((decode_mfma_kernel<D, 16, KV, true>), dim3(grid), dim3(64 * wpg), lds,
                      stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool I8>
+template <int D, int KV>
 hipError_t dispatch_group(const DecodeParams& p, hipStream_t stream) {
   switch (p.q_heads / p.kv_heads) {
-    case 4: return launch_one<D, 4, I8>(p, stream);
-    case 8: return launch_one<D, 8, I8>(p, stream);
-    case 16: return launch_one<D, 16, I8>(p, stream);
+    case 4: return launch_one<D, 4, KV>(p, stream);
+    case 8: return launch_one<D, 8, KV>(p, stream);
+    case 16: return launch_one<D, 16, KV>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t dispatch_format(const DecodeParams& p, int kv, hipStream_t stream) {
+  switch (kv) {
+    case kKvF16: return dispatch_group<D, kKvF16>(p, stream);
+    case kKvI8: return dispatch_group<D, kKvI8>(p, stream);
+    case kKvF8: return dispatch_group<D, kKvF8>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t prefix_format(const DecodeParams& p, int kv, hipStream_t stream) {
+  switch (kv) {
+    case kKvF16: return launch_prefix<D, kKvF16>(p, stream);
+    case kKvI8: return launch_prefix<D, kKvI8>(p, stream);
+    case kKvF8: return launch_prefix<D, kKvF8>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefix_mfma(const DecodeParams& p, bool int8, hipStream_t stream) {
-  if (p.head_dim == 128) return int8 ? launch_prefix<128, true>(p, stream) : launch_prefix<128, false>(p, stream);
-  if (p.head_dim == 64) return int8 ? launch_prefix<64, true>(p, stream) : launch_prefix<64, false>(p, stream);
+hipError_t launch_prefix_mfma(const DecodeParams& p, int kv, hipStream_t stream) {
+  if (p.head_dim == 128) return prefix_format<128>(p, kv, stream);
+  if (p.head_dim == 64) return prefix_format<64>(p, kv, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode_mfma(const DecodeParams& p, bool int8, hipStream_t stream) {
-  if (p.head_dim == 128)
-    return int8 ? dispatch_group<128, true>(p, stream) : dispatch_group<128, false>(p, stream);
-  if (p.head_dim == 64)
-    return int8 ? dispatch_group<64, true>(p, stream) : dispatch_group<64, false>(p, stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv, hipStream_t stream) {
+  if (p.head_dim == 128) return dispatch_format<128>(p, kv, stream);
+  if (p.head_dim == 64) return dispatch_format<64>(p, kv, stream);
   return hipErrorInvalidValue;
 }
 

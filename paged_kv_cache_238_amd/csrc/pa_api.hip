@@ -83,14 +83,14 @@ int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 // Shared body of the decode entry points.  mode: 0 = full decode (direct
 // when one partition, else partials + merge), 1 = partials only.
 int decode_common(int mode, void* out, float* lse_out, const void* q, const void* k_pool,
-                  const void* v_pool, const float* k_scale, const float* v_scale, bool int8,
+                  const void* v_pool, const float* k_scale, const float* v_scale, int kv,
                   const int32_t* block_table, int max_blocks, const int32_t* context_lens,
                   int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
                   int block_size, int num_blocks, float scale, int partition_size,
                   void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_pool || !v_pool || !block_table || !context_lens) return PA_ERR_NULL;
   if (mode == 0 && !out) return PA_ERR_NULL;
-  if (int8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (kv != pa::kKvF16 && (!k_scale || !v_scale)) return PA_ERR_NULL;
   int st = check_decode_shapes(max_blocks, max_context_len, batch, q_heads, kv_heads, head_dim,
                                block_size, num_blocks, partition_size);
   if (st != PA_OK) return st;
@@ -133,7 +133,7 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   p.direct = direct ? 1 : 0;
   p.target_waves = PA_TARGET_WAVES;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = status_of(pa::launch_decode(p, int8, s));
+  st = status_of(pa::launch_decode(p, kv, s));
   if (st != PA_OK || direct || mode == 1) return st;
 
   pa::MergeParams mp = {};
@@ -197,13 +197,13 @@ int check_prefix(int max_context_len, int prefix_len) {
 // partials over the suffixes, records over the prefix for all queries at
 // once, then one merge of both.
 int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
-                  const void* v_pool, const float* k_scale, const float* v_scale, bool int8,
+                  const void* v_pool, const float* k_scale, const float* v_scale, int kv,
                   const int32_t* block_table, int max_blocks, const int32_t* context_lens,
                   int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
                   int block_size, int num_blocks, float scale, int prefix_len, void* workspace,
                   size_t workspace_bytes, void* stream) {
   if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens) return PA_ERR_NULL;
-  if (int8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (kv != pa::kKvF16 && (!k_scale || !v_scale)) return PA_ERR_NULL;
   int st = check_decode_shapes(max_blocks, max_context_len, batch, q_heads, kv_heads, head_dim,
                                block_size, num_blocks, 0);
   if (st != PA_OK) return st;
@@ -253,7 +253,7 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   ps.max_blocks = max_blocks - prefix_len / kBlockTokens;
   ps.max_context_len = suf_max;
   ps.n_part = n_suf;
-  st = status_of(pa::launch_decode(ps, int8, s));
+  st = status_of(pa::launch_decode(ps, kv, s));
   if (st != PA_OK) return st;
 
   // Prefix: one record per (sequence, query head, prefix partition).
@@ -265,7 +265,7 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   pp.partition_size = P_pre;
   pp.n_part = n_pre;
   pp.prefix_tiles = tiles;
-  st = status_of(pa::launch_prefix_mfma(pp, int8, s));
+  st = status_of(pa::launch_prefix_mfma(pp, kv, s));
   if (st != PA_OK) return st;
 
   pa::MergeParams mp = {};
@@ -336,10 +336,13 @@ int pa_write_kv(const void* k_new, const void* v_new, const int32_t* slot_mappin
   return status_of(pa::launch_write_kv(p, static_cast<hipStream_t>(stream)));
 }
 
-int pa_write_kv_int8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
-                     int8_t* k_pool, int8_t* v_pool, float* k_scale, float* v_scale,
-                     int num_tokens, int num_blocks, int block_size, int kv_heads, int head_dim,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+int write_q8(bool fp8, const void* k_new, const void* v_new, const int32_t* slot_mapping,
+             void* k_pool, void* v_pool, float* k_scale, float* v_scale, int num_tokens,
+             int num_blocks, int block_size, int kv_heads, int head_dim, void* stream) {
   int st = check_write(k_new, v_new, slot_mapping, k_pool, v_pool, num_tokens, num_blocks,
                        block_size, kv_heads, head_dim);
   if (st != PA_OK) return st;
@@ -357,7 +360,28 @@ int pa_write_kv_int8(const void* k_new, const void* v_new, const int32_t* slot_m
   p.kv_heads = kv_heads;
   p.head_dim = head_dim;
   p.capacity = (long long)num_blocks * kBlockTokens;
-  return status_of(pa::launch_write_kv_int8(p, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(fp8 ? pa::launch_write_kv_fp8(p, s) : pa::launch_write_kv_int8(p, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_write_kv_int8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                     int8_t* k_pool, int8_t* v_pool, float* k_scale, float* v_scale,
+                     int num_tokens, int num_blocks, int block_size, int kv_heads, int head_dim,
+                     void* stream) {
+  return write_q8(false, k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale,
+                  num_tokens, num_blocks, block_size, kv_heads, head_dim, stream);
+}
+
+int pa_write_kv_fp8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                    uint8_t* k_pool, uint8_t* v_pool, float* k_scale, float* v_scale,
+                    int num_tokens, int num_blocks, int block_size, int kv_heads, int head_dim,
+                    void* stream) {
+  return write_q8(true, k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale,
+                  num_tokens, num_blocks, block_size, kv_heads, head_dim, stream);
 }
 
 int pa_decode_partition_size(int batch, int q_heads, int kv_heads, int head_dim,
@@ -381,7 +405,7 @@ int pa_decode(void* out, float* lse_out, const void* q, const void* k_pool, cons
               int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
               int block_size, int num_blocks, float scale, int partition_size, void* workspace,
               size_t workspace_bytes, void* stream) {
-  return decode_common(0, out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_table,
+  return decode_common(0, out, lse_out, q, k_pool, v_pool, nullptr, nullptr, pa::kKvF16, block_table,
                        max_blocks, context_lens, max_context_len, batch, q_heads, kv_heads,
                        head_dim, block_size, num_blocks, scale, partition_size, workspace,
                        workspace_bytes, stream);
@@ -393,10 +417,22 @@ int pa_decode_int8(void* out, float* lse_out, const void* q, const int8_t* k_poo
                    int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
                    int block_size, int num_blocks, float scale, int partition_size,
                    void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(0, out, lse_out, q, k_pool, v_pool, k_scale, v_scale, true, block_table,
+  return decode_common(0, out, lse_out, q, k_pool, v_pool, k_scale, v_scale, pa::kKvI8, block_table,
                        max_blocks, context_lens, max_context_len, batch, q_heads, kv_heads,
                        head_dim, block_size, num_blocks, scale, partition_size, workspace,
                        workspace_bytes, stream);
+}
+
+int pa_decode_fp8(void* out, float* lse_out, const void* q, const uint8_t* k_pool,
+                  const uint8_t* v_pool, const float* k_scale, const float* v_scale,
+                  const int32_t* block_table, int max_blocks, const int32_t* context_lens,
+                  int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
+                  int block_size, int num_blocks, float scale, int partition_size,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(0, out, lse_out, q, k_pool, v_pool, k_scale, v_scale, pa::kKvF8,
+                       block_table, max_blocks, context_lens, max_context_len, batch, q_heads,
+                       kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
+                       workspace, workspace_bytes, stream);
 }
 
 int pa_decode_partials(const void* q, const void* k_pool, const void* v_pool,
@@ -404,7 +440,7 @@ int pa_decode_partials(const void* q, const void* k_pool, const void* v_pool,
                        int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
                        int block_size, int num_blocks, float scale, int partition_size,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(1, nullptr, nullptr, q, k_pool, v_pool, nullptr, nullptr, false,
+  return decode_common(1, nullptr, nullptr, q, k_pool, v_pool, nullptr, nullptr, pa::kKvF16,
                        block_table, max_blocks, context_lens, max_context_len, batch, q_heads,
                        kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
                        workspace, workspace_bytes, stream);
@@ -417,7 +453,7 @@ int pa_decode_partials_int8(const void* q, const int8_t* k_pool, const int8_t* v
                             int q_heads, int kv_heads, int head_dim, int block_size,
                             int num_blocks, float scale, int partition_size, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  return decode_common(1, nullptr, nullptr, q, k_pool, v_pool, k_scale, v_scale, true,
+  return decode_common(1, nullptr, nullptr, q, k_pool, v_pool, k_scale, v_scale, pa::kKvI8,
                        block_table, max_blocks, context_lens, max_context_len, batch, q_heads,
                        kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
                        workspace, workspace_bytes, stream);
@@ -443,7 +479,7 @@ int pa_decode_shared_prefix(void* out, float* lse_out, const void* q, const void
                             int q_heads, int kv_heads, int head_dim, int block_size,
                             int num_blocks, float scale, int prefix_len, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  return prefix_common(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, false, block_table,
+  return prefix_common(out, lse_out, q, k_pool, v_pool, nullptr, nullptr, pa::kKvF16, block_table,
                        max_blocks, context_lens, max_context_len, batch, q_heads, kv_heads,
                        head_dim, block_size, num_blocks, scale, prefix_len, workspace,
                        workspace_bytes, stream);
@@ -457,9 +493,36 @@ int pa_decode_shared_prefix_int8(void* out, float* lse_out, const void* q, const
                                  int head_dim, int block_size, int num_blocks, float scale,
                                  int prefix_len, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  return prefix_common(out, lse_out, q, k_pool, v_pool, k_scale, v_scale, true, block_table,
+  return prefix_common(out, lse_out, q, k_pool, v_pool, k_scale, v_scale, pa::kKvI8, block_table,
                        max_blocks, context_lens, max_context_len, batch, q_heads, kv_heads,
                        head_dim, block_size, num_blocks, scale, prefix_len, workspace,
+                       workspace_bytes, stream);
+}
+
+int pa_decode_partials_fp8(const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, int max_blocks,
+                           const int32_t* context_lens, int max_context_len, int batch,
+                           int q_heads, int kv_heads, int head_dim, int block_size,
+                           int num_blocks, float scale, int partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return decode_common(1, nullptr, nullptr, q, k_pool, v_pool, k_scale, v_scale, pa::kKvF8,
+                       block_table, max_blocks, context_lens, max_context_len, batch, q_heads,
+                       kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
+                       workspace, workspace_bytes, stream);
+}
+
+int pa_decode_shared_prefix_fp8(void* out, float* lse_out, const void* q, const uint8_t* k_pool,
+                                const uint8_t* v_pool, const float* k_scale,
+                                const float* v_scale, const int32_t* block_table,
+                                int max_blocks, const int32_t* context_lens,
+                                int max_context_len, int batch, int q_heads, int kv_heads,
+                                int head_dim, int block_size, int num_blocks, float scale,
+                                int prefix_len, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return prefix_common(out, lse_out, q, k_pool, v_pool, k_scale, v_scale, pa::kKvF8,
+                       block_table, max_blocks, context_lens, max_context_len, batch, q_heads,
+                       kv_heads, head_dim, block_size, num_blocks, scale, prefix_len, workspace,
                        workspace_bytes, stream);
 }
 

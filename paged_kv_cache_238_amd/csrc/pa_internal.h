@@ -10,12 +10,20 @@ namespace pa {
 
 constexpr int kBlockTokens = 16;   // tokens per physical KV block
 
+// KV cache element formats.  The 8-bit ones carry fp32 scales per (token,
+// kv head), laid out [num_blocks, kv_heads, 16].
+enum : int {
+  kKvF16 = 0,   // fp16 values
+  kKvI8 = 1,    // int8 codes
+  kKvF8 = 2,    // OCP FP8 E4M3 codes
+};
+
 // Everything one decode launch needs.  Pointers are device pointers.
 struct DecodeParams {
   const uint16_t* q;          // fp16 [B, Hq, D]
-  const void* k_pool;         // fp16 or int8 [NB, 16, Hkv, D]
+  const void* k_pool;         // fp16, int8 or fp8 [NB, 16, Hkv, D]
   const void* v_pool;
-  const float* k_scale;       // int8 only: fp32 [NB, Hkv, 16]
+  const float* k_scale;       // 8-bit pools only: fp32 [NB, Hkv, 16]
   const float* v_scale;
   const int32_t* block_table; // [B, max_blocks]
   const int32_t* context_lens;// [B]
@@ -66,7 +74,7 @@ struct WriteParams {
   const int32_t* slots;       // [T]
   void* k_pool;
   void* v_pool;
-  float* k_scale;             // int8 pools only
+  float* k_scale;             // 8-bit pools only
   float* v_scale;
   int num_tokens, kv_heads, head_dim;
   long long capacity;         // num_blocks * 16 slots
@@ -86,16 +94,17 @@ inline unsigned decode_workgroups(const DecodeParams& p, int wpg) {
   return (unsigned)(full < bound ? full : bound);
 }
 
-// Launchers return hipSuccess or the launch error.  `int8` selects the
-// int8-cache instantiation.
+// Launchers return hipSuccess or the launch error.  `kv` is the cache
+// format (kKvF16, kKvI8, kKvF8).
 // Group size 1 or 2: VALU kernel; 4, 8 or 16: matrix-core kernel.
-hipError_t launch_decode(const DecodeParams& p, bool int8, hipStream_t stream);
-hipError_t launch_decode_valu(const DecodeParams& p, bool int8, hipStream_t stream);
-hipError_t launch_decode_mfma(const DecodeParams& p, bool int8, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int kv, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeParams& p, int kv, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv, hipStream_t stream);
 // Shared prefix: records of every (sequence, query head) over the prefix.
-hipError_t launch_prefix_mfma(const DecodeParams& p, bool int8, hipStream_t stream);
+hipError_t launch_prefix_mfma(const DecodeParams& p, int kv, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_write_kv(const WriteParams& p, hipStream_t stream);
 hipError_t launch_write_kv_int8(const WriteParams& p, hipStream_t stream);
+hipError_t launch_write_kv_fp8(const WriteParams& p, hipStream_t stream);
 
 }  // namespace pa

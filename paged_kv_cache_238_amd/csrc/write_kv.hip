@@ -13,6 +13,11 @@
 // the way in, following KVCacheQuantizer.quantize's per_channel branch in the
 // same discosf.com section: scale = absmax / 127 in fp32 (zero -> 1.0),
 // code = clip(round-half-even(x / scale), -128, 127), fp32 IEEE division.
+//
+// The FP8 write (OCP E4M3, the other 8-bit precision "二、优化方向" of the
+// discosf.com article names) applies the same per-row rule with E4M3's
+// largest finite value: scale = absmax / 448, code = the E4M3 value nearest
+// to x / scale, ties to the even code, saturating at +-448.
 #include "pa_internal.h"
 
 namespace pa {
@@ -36,9 +41,40 @@ __global__ __launch_bounds__(kThreads) void write_kv_f16_kernel(const WriteParam
   }
 }
 
+// Nearest OCP E4M3 code to a finite fp32 value: ties to the even code,
+// magnitudes at or above 448 saturate to 448 (0x7E); the sign bit is y's.
+__device__ __forceinline__ uint8_t e4m3_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t mag;
+  if (!(a < 448.0f)) {
+    mag = 0x7E;
+  } else if (a < 0.015625f) {
+    // below the smallest normal 2^-6 the codes are the multiples of 2^-9
+    // (8 * 2^-9 is the smallest normal, code 0x08)
+    mag = (uint32_t)rintf(a * 512.0f);
+  } else {
+    const uint32_t au = u & 0x7FFFFFFFu;
+    uint32_t e = (au >> 23) - 127u + 7u;     // biased E4M3 exponent, 1 .. 15
+    uint32_t m = (au >> 20) & 7u;            // top three mantissa bits
+    const uint32_t rest = au & 0xFFFFFu;     // the 20 bits dropped
+    if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) {
+      if (++m == 8u) {
+        m = 0;
+        ++e;
+      }
+    }
+    mag = (e << 3) | m;
+    if (mag > 0x7Eu) mag = 0x7E;
+  }
+  return (uint8_t)(sign | mag);
+}
+
 // One wave per (token, kv head) row; lane holds D/64 consecutive elements.
-template <int D>
-__device__ __forceinline__ void quantise_row(const uint16_t* src, int8_t* dst, float* scale_dst,
+// FP8 = false: int8 codes; true: E4M3 codes.
+template <int D, bool FP8>
+__device__ __forceinline__ void quantise_row(const uint16_t* src, uint8_t* dst, float* scale_dst,
                                              int lane) {
   constexpr int PER = D / 64;
   float x[PER];
@@ -52,19 +88,23 @@ __device__ __forceinline__ void quantise_row(const uint16_t* src, int8_t* dst, f
   for (int e = 0; e < PER; ++e) amax = fmaxf(amax, fabsf(x[e]));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  float s = __fdiv_rn(amax, 127.0f);
+  float s = __fdiv_rn(amax, FP8 ? 448.0f : 127.0f);
   s = (s > 0.f) ? s : 1.0f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    float qv = rintf(__fdiv_rn(x[e], s));
-    qv = fminf(fmaxf(qv, -128.f), 127.f);
-    dst[lane * PER + e] = (int8_t)(int)qv;
+    const float y = __fdiv_rn(x[e], s);
+    if constexpr (FP8) {
+      dst[lane * PER + e] = e4m3_code(y);
+    } else {
+      const float qv = fminf(fmaxf(rintf(y), -128.f), 127.f);
+      dst[lane * PER + e] = (uint8_t)(int8_t)(int)qv;
+    }
   }
   if (lane == 0) *scale_dst = s;
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(const WriteParams p) {
+template <int D, bool FP8>
+__global__ __launch_bounds__(kThreads) void write_kv_q8_kernel(const WriteParams p) {
   const int lane = threadIdx.x & 63;
   const long long rowid = (long long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (rowid >= (long long)p.num_tokens * p.kv_heads) return;
@@ -74,8 +114,10 @@ __global__ __launch_bounds__(kThreads) void write_kv_i8_kernel(const WriteParams
   const size_t src = ((size_t)tok * p.kv_heads + g) * D;
   const size_t dst = ((size_t)slot * p.kv_heads + g) * D;
   const size_t sdst = ((size_t)(slot / 16) * p.kv_heads + g) * 16 + slot % 16;   // [NB, Hkv, 16]
-  quantise_row<D>(p.k_new + src, static_cast<int8_t*>(p.k_pool) + dst, p.k_scale + sdst, lane);
-  quantise_row<D>(p.v_new + src, static_cast<int8_t*>(p.v_pool) + dst, p.v_scale + sdst, lane);
+  quantise_row<D, FP8>(p.k_new + src, static_cast<uint8_t*>(p.k_pool) + dst, p.k_scale + sdst,
+                       lane);
+  quantise_row<D, FP8>(p.v_new + src, static_cast<uint8_t*>(p.v_pool) + dst, p.v_scale + sdst,
+                       lane);
 }
 
 }  // namespace
@@ -88,17 +130,30 @@ hipError_t launch_write_kv(const WriteParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_write_kv_int8(const WriteParams& p, hipStream_t stream) {
+namespace {
+
+template <bool FP8>
+hipError_t launch_q8(const WriteParams& p, hipStream_t stream) {
   if (p.num_tokens == 0) return hipSuccess;
   const long long rows = (long long)p.num_tokens * p.kv_heads;
   dim3 grid((unsigned)((rows + 3) / 4));
   if (p.head_dim == 128)
-    hipLaunchKernelGGL(write_kv_i8_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((write_kv_q8_kernel<128, FP8>), grid, dim3(kThreads), 0, stream, p);
   else if (p.head_dim == 64)
-    hipLaunchKernelGGL(write_kv_i8_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((write_kv_q8_kernel<64, FP8>), grid, dim3(kThreads), 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_write_kv_int8(const WriteParams& p, hipStream_t stream) {
+  return launch_q8<false>(p, stream);
+}
+
+hipError_t launch_write_kv_fp8(const WriteParams& p, hipStream_t stream) {
+  return launch_q8<true>(p, stream);
 }
 
 }  // namespace pa

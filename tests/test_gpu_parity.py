@@ -61,10 +61,11 @@ def gpu_decode(pa, wl, d, partition_size=0, return_lse=True, table=None, k=None,
     kp = d["k_pool"] if k is None else k
     vp = d["v_pool"] if v is None else v
     bt = d["block_table"] if table is None else table
-    if wl.kv_dtype == "int8":
-        return pa.decode_int8(d["q"], kp, vp, d["k_scale"], d["v_scale"], bt, d["context_lens"],
-                              scale=wl.scale, partition_size=partition_size,
-                              max_context_len=wl.max_context_len, return_lse=return_lse)
+    if wl.kv_dtype in ("int8", "fp8"):
+        fn = pa.decode_int8 if wl.kv_dtype == "int8" else pa.decode_fp8
+        return fn(d["q"], kp, vp, d["k_scale"], d["v_scale"], bt, d["context_lens"],
+                  scale=wl.scale, partition_size=partition_size,
+                  max_context_len=wl.max_context_len, return_lse=return_lse)
     return pa.decode(d["q"], kp, vp, bt, d["context_lens"], scale=wl.scale,
                      partition_size=partition_size, max_context_len=wl.max_context_len,
                      return_lse=return_lse)
@@ -131,6 +132,69 @@ def test_write_kv_int8_matches_oracle_quantiser(pa):
         assert np.array_equal(ds.cpu().numpy().view(np.uint32), want_s.view(np.uint32)), which
 
 
+def test_write_kv_fp8_matches_oracle_quantiser(pa):
+    """The FP8 write is bit-exact (codes and scales) against the oracle's
+    E4M3 quantiser, including rows that hit ties, the smallest subnormals,
+    saturation at 448 and zero rows."""
+    rng = np.random.default_rng(18)
+    NB, Hkv, D, T = 6, 4, 128, 40
+    x = rng.standard_normal((2, T, Hkv, D), dtype=np.float32).astype(np.float16)
+    x[0, 3, 1] = 0                                   # zero row -> scale 1
+    x[1, 5] *= np.float16(40)
+    # absmax 448 (scale 1): every value below is exact in fp16 and several
+    # sit exactly between two E4M3 neighbours
+    row = np.array([448, 1.0625, 1.1875, -3 * 2.0 ** -10, 2.0 ** -10, 232, 240, -448,
+                    7.5 * 2.0 ** -9, 2.0 ** -9, -0.0, 0.3], np.float16)
+    x[0, 9, 2, :row.size] = row
+    x[0, 9, 2, row.size:] = 0
+    # magnitudes 2^-12 .. 2^8 in one row: codes across every binade, subnormals included
+    x[1, 11, 0] = (2.0 ** np.linspace(-12, 8, D) * np.sign(x[1, 11, 0])).astype(np.float16)
+    slots = rng.permutation(NB * 16)[:T].astype(np.int32)
+    slots[7] = -1
+    kp = np.zeros((NB, 16, Hkv, D), np.uint8)
+    ks = np.full((NB, Hkv, 16), -1.0, np.float32)
+    dk, dv, dks, dvs = t(kp), t(kp), t(ks), t(ks)
+    pa.write_kv_fp8(t(x[0]), t(x[1]), t(slots), dk, dv, dks, dvs)
+    for which, src, dp, ds in ((0, x[0], dk, dks), (1, x[1], dv, dvs)):
+        codes, sc = ref.ref_quantize_fp8(src)
+        want_p, want_s = kp.copy(), ks.copy()
+        for i, s in enumerate(slots):
+            if s >= 0:
+                want_p[s // 16, s % 16] = codes[i]
+                want_s[s // 16, :, s % 16] = sc[i]
+        got = dp.cpu().numpy()
+        bad = np.argwhere(got != want_p)
+        assert bad.size == 0, (which, bad[:5], got[tuple(bad[0])] if bad.size else None)
+        assert np.array_equal(ds.cpu().numpy().view(np.uint32), want_s.view(np.uint32)), which
+
+
+@pytest.mark.parametrize("G", [1, 8])
+def test_fp8_every_code_decodes_exactly(pa, G):
+    """One-token contexts with unit scales return V itself, so every E4M3
+    code's decoded value shows in the output exactly (both kernels); the two
+    NaN codes give NaN.  (Code 0x80, -0, comes out as +0: the accumulator
+    starts at +0.)"""
+    D, B = 128, 2
+    codes = np.arange(256, dtype=np.uint8).reshape(B, D)
+    NB = 4
+    vp = np.zeros((NB, 16, 1, D), np.uint8)
+    vp[1, 0, 0] = codes[0]
+    vp[3, 0, 0] = codes[1]
+    kp = np.zeros((NB, 16, 1, D), np.uint8)
+    ones = np.ones((NB, 1, 16), np.float32)
+    bt = np.array([[1], [3]], np.int32)
+    cl = np.array([1, 1], np.int32)
+    q = np.random.default_rng(3).standard_normal((B, G, D), dtype=np.float32).astype(np.float16)
+    out = pa.decode_fp8(t(q), t(kp), t(vp), t(ones), t(ones), t(bt), t(cl), max_context_len=1)
+    out = out.cpu().numpy().astype(np.float64)
+    want = ref.fp8_e4m3_to_float(codes)
+    for h in range(G):
+        got = out[:, h, :]
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], want[~nan])
+
+
 # --------------------------------------------------------------------------- decode
 
 def test_tiny_step_write_then_decode(pa):
@@ -150,7 +214,8 @@ def test_tiny_step_write_then_decode(pa):
     np.testing.assert_allclose(lse.cpu().numpy(), want_lse, rtol=0, atol=1e-4)
 
 
-SMALL_CASES = [(n, P) for n in ("llama2_7b", "gqa70b_mixed", "prefix_shared", "long128k_int8")
+SMALL_CASES = [(n, P) for n in ("llama2_7b", "gqa70b_mixed", "prefix_shared", "long128k_int8",
+                                 "long128k_fp8")
                for P in (0, 16, 64, 512)]
 
 
@@ -167,25 +232,28 @@ def test_small_configs_vs_oracle(pa, name, P):
     np.testing.assert_allclose(lse.cpu().numpy(), want_lse, rtol=0, atol=1e-4)
 
 
-@pytest.mark.parametrize("G,D,int8", [(g, d, i) for g in (1, 2, 4, 8, 16) for d in (64, 128)
-                                      for i in (False, True)])
-def test_group_and_head_dim_matrix(pa, G, D, int8):
+KV_DTYPES = ("fp16", "int8", "fp8")
+
+
+@pytest.mark.parametrize("G,D,kv", [(g, d, k) for g in (1, 2, 4, 8, 16) for d in (64, 128)
+                                    for k in KV_DTYPES])
+def test_group_and_head_dim_matrix(pa, G, D, kv):
     """Every supported (group, head_dim, cache dtype) with ragged lengths that
     cover empty-looking tails, one token, exact block multiples and several
     partitions."""
     Hkv = 2
     over = dict(batch=5, q_heads=G * Hkv, kv_heads=Hkv, head_dim=D, lmin=1, lmax=700,
-                occupancy=0.9, kv_dtype="int8" if int8 else "fp16")
-    wl = gen.make("gqa70b_mixed", seed=500 + G * 3 + D + int8, overrides=over)
+                occupancy=0.9, kv_dtype=kv)
+    wl = gen.make("gqa70b_mixed", seed=500 + G * 3 + D + KV_DTYPES.index(kv), overrides=over)
     wl.context_lens[:3] = [1, 16, 513]
     wl = _rebuild_table(wl)
     vals = gen.fill_numpy(wl, new_slot_poison=False)
-    say(f"matrix G={G} D={D} int8={int8} lens={wl.context_lens.tolist()}")
+    say(f"matrix G={G} D={D} kv={kv} lens={wl.context_lens.tolist()}")
     d = device_inputs(wl, vals)
     for P in (0, 128):
         out = gpu_decode(pa, wl, d, partition_size=P, return_lse=False)
         want, _ = oracle_decode(wl, vals)
-        check_close(out.cpu().numpy(), want, f"G={G} D={D} int8={int8} P={P}")
+        check_close(out.cpu().numpy(), want, f"G={G} D={D} kv={kv} P={P}")
 
 
 def _rebuild_table(wl):
@@ -315,13 +383,13 @@ def test_bad_metadata_gives_nan_rows_not_faults(pa):
 
 # --------------------------------------------------------------------------- full sizes
 
-FULL = ["llama2_7b", "gqa70b_mixed", "prefix_shared", "long128k_int8"]
+FULL = ["llama2_7b", "gqa70b_mixed", "prefix_shared", "long128k_int8", "long128k_fp8"]
 
 
 def _host_copy(wl, d):
     v = {"q": d["q"].cpu().numpy(), "k_pool": d["k_pool"].cpu().numpy(),
          "v_pool": d["v_pool"].cpu().numpy()}
-    if wl.kv_dtype == "int8":
+    if wl.kv_dtype in ("int8", "fp8"):
         v["k_scale"] = d["k_scale"].cpu().numpy()
         v["v_scale"] = d["v_scale"].cpu().numpy()
     return v

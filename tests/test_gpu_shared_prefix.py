@@ -24,7 +24,7 @@ def pa():
 
 
 def run_prefix(pa, wl, d, prefix_len, return_lse=True):
-    if wl.kv_dtype == "int8":
+    if wl.kv_dtype in ("int8", "fp8"):
         return pa.decode_shared_prefix(d["q"], d["k_pool"], d["v_pool"], d["block_table"],
                                        d["context_lens"], prefix_len, scale=wl.scale,
                                        max_context_len=wl.max_context_len,
@@ -45,7 +45,7 @@ def prefix_len_of(wl):
     return n * 16
 
 
-@pytest.mark.parametrize("kv_dtype", ["fp16", "int8"])
+@pytest.mark.parametrize("kv_dtype", ["fp16", "int8", "fp8"])
 def test_small_prefix_workload_vs_oracle(pa, kv_dtype):
     wl = gen.make("prefix_shared", small=True, overrides=dict(kv_dtype=kv_dtype))
     vals = gen.fill_numpy(wl, new_slot_poison=False)
@@ -59,22 +59,23 @@ def test_small_prefix_workload_vs_oracle(pa, kv_dtype):
     np.testing.assert_allclose(lse.cpu().numpy(), want_lse, rtol=0, atol=1e-4)
 
 
-@pytest.mark.parametrize("G,D,int8", [(1, 64, False), (2, 128, True), (4, 128, False),
-                                      (8, 64, True), (16, 128, False)])
-def test_query_tiles_and_groups(pa, G, D, int8):
+@pytest.mark.parametrize("G,D,kv", [(1, 64, "fp16"), (2, 128, "int8"), (4, 128, "fp16"),
+                                    (8, 64, "int8"), (16, 128, "fp16"), (1, 128, "fp8"),
+                                    (8, 128, "fp8")])
+def test_query_tiles_and_groups(pa, G, D, kv):
     """Query tiles of 16 cut across sequences and heads (batch * G not a
     multiple of 16), every supported group size; prefix of 3 blocks."""
     over = dict(batch=7, q_heads=G * 2, kv_heads=2, head_dim=D, prefix=48, smin=1, smax=300,
-                kv_dtype="int8" if int8 else "fp16")
-    wl = gen.make("prefix_shared", seed=40 + G + D + int8, small=True, overrides=over)
+                kv_dtype=kv)
+    wl = gen.make("prefix_shared", seed=40 + G + D + len(kv), small=True, overrides=over)
     vals = gen.fill_numpy(wl, new_slot_poison=False)
     pre = prefix_len_of(wl)
     assert pre == 48
     d = device_inputs(wl, vals)
-    say(f"tiles G={G} D={D} int8={int8} lens={wl.context_lens.tolist()}")
+    say(f"tiles G={G} D={D} kv={kv} lens={wl.context_lens.tolist()}")
     out = run_prefix(pa, wl, d, pre, return_lse=False)
     want, _ = oracle_decode(wl, vals)
-    check_close(out.cpu().numpy(), want, f"tiles G={G} D={D} int8={int8}")
+    check_close(out.cpu().numpy(), want, f"tiles G={G} D={D} kv={kv}")
 
 
 def test_prefix_shorter_than_shared_part_and_empty_suffixes(pa):

@@ -1,8 +1,8 @@
 """Seeded synthetic inputs for paged-attention decode over a block-paged KV cache.
 
 This module only *draws inputs*: context lengths, block tables, new-token
-slots, and Q / K / V values (fp16, or int8 codes plus fp32 per-(token, kv-head)
-scales, laid out [num_blocks, kv_heads, 16]).  It computes none of the attention, quantisation or KV-write
+slots, and Q / K / V values (fp16, or int8 / fp8 codes plus fp32
+per-(token, kv-head) scales, laid out [num_blocks, kv_heads, 16]).  It computes none of the attention, quantisation or KV-write
 arithmetic, so the CPU oracle side and the GPU side of a test can both take
 their inputs from here without sharing any of the method.
 
@@ -23,9 +23,12 @@ Recipe (seed = 2380 + config index unless given):
   then values in the order q, k_pool, v_pool, k_new, v_new, each
   rng.standard_normal(dtype=float32).astype(float16).  int8 pools draw codes
   uniformly from [-127, 127] and scales uniformly from [2.3/127, 3.8/127]
-  (the range of absmax/127 for 128 N(0,1) values).  Poisoned runs fill every
+  (the range of absmax/127 for 128 N(0,1) values).  fp8 pools (OCP E4M3,
+  stored as raw uint8 codes) draw codes uniformly from the 254 finite codes
+  (every code but 0x7F and 0xFF) and scales from [2.3/448, 3.8/448].  Poisoned runs fill every
   block no table references and every tail slot (token >= L in a sequence's
-  last block) with fp16 NaN (int8 pools: NaN scales), so a stray read shows.
+  last block) with fp16 NaN (int8 / fp8 pools: NaN scales), so a stray read
+  shows.
   The torch backend draws the same kind of values on the device with a seeded
   torch.Generator (used for full-size workloads; values differ from numpy's).
 """
@@ -58,6 +61,10 @@ SPECS: dict[str, dict[str, Any]] = {
     "long128k_int8": dict(idx=5, batch=4, q_heads=64, kv_heads=8, head_dim=128,
                           kv_dtype="int8", ctx=131072, scatter=0.15,
                           partition_size=512),
+    # the same 128K-token decode over an FP8 (E4M3) cache
+    "long128k_fp8": dict(idx=6, batch=4, q_heads=64, kv_heads=8, head_dim=128,
+                         kv_dtype="fp8", ctx=131072, scatter=0.15,
+                         partition_size=512),
 }
 
 # Scaled-down twins used for element-by-element parity (same structure,
@@ -67,9 +74,14 @@ SMALL: dict[str, dict[str, Any]] = {
     "gqa70b_mixed": dict(batch=8, q_heads=16, kv_heads=2, lmin=1, lmax=1500),
     "prefix_shared": dict(batch=6, q_heads=4, kv_heads=4, prefix=128, smin=1, smax=100),
     "long128k_int8": dict(batch=2, q_heads=16, kv_heads=2, ctx=3000, partition_size=512),
+    "long128k_fp8": dict(batch=2, q_heads=16, kv_heads=2, ctx=3000, partition_size=512),
 }
 
-ORDER = ["tiny_gqa", "llama2_7b", "gqa70b_mixed", "prefix_shared", "long128k_int8"]
+ORDER = ["tiny_gqa", "llama2_7b", "gqa70b_mixed", "prefix_shared", "long128k_int8",
+         "long128k_fp8"]
+
+# the 254 finite OCP E4M3 codes (0x7F and 0xFF are NaN)
+FP8_FINITE_CODES = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
 
 
 def cdiv(a: int, b: int) -> int:
@@ -85,7 +97,7 @@ class Workload:
     head_dim: int
     num_blocks: int
     max_blocks: int
-    kv_dtype: str                     # "fp16" or "int8"
+    kv_dtype: str                     # "fp16", "int8" or "fp8"
     scale: float
     partition_size: int               # 0 = library's choice
     context_lens: np.ndarray          # int32 [B]
@@ -152,7 +164,7 @@ def make(name: str, seed: int | None = None, *, small: bool = False,
             pos += n
         used_n = pos
         spare = perm[used_n:]
-    elif name in ("llama2_7b", "long128k_int8"):
+    elif name in ("llama2_7b", "long128k_int8", "long128k_fp8"):
         ctx = spec["ctx"]
         per = cdiv(ctx, BLOCK)
         maxb = spec.get("max_blocks", per)
@@ -262,6 +274,11 @@ def fill_numpy(wl: Workload, *, new_slot_poison: bool = True) -> dict[str, np.nd
     if wl.kv_dtype == "fp16":
         v["k_pool"] = _normal16(rng, (NB, BLOCK, Hkv, D))
         v["v_pool"] = _normal16(rng, (NB, BLOCK, Hkv, D))
+    elif wl.kv_dtype == "fp8":
+        v["k_pool"] = rng.choice(FP8_FINITE_CODES, size=(NB, BLOCK, Hkv, D))
+        v["v_pool"] = rng.choice(FP8_FINITE_CODES, size=(NB, BLOCK, Hkv, D))
+        v["k_scale"] = rng.uniform(2.3 / 448, 3.8 / 448, size=(NB, Hkv, BLOCK)).astype(np.float32)
+        v["v_scale"] = rng.uniform(2.3 / 448, 3.8 / 448, size=(NB, Hkv, BLOCK)).astype(np.float32)
     else:
         v["k_pool"] = rng.integers(-127, 128, size=(NB, BLOCK, Hkv, D), dtype=np.int8)
         v["v_pool"] = rng.integers(-127, 128, size=(NB, BLOCK, Hkv, D), dtype=np.int8)
@@ -310,6 +327,15 @@ def fill_torch(wl: Workload, device, *, chunk_rows: int = 1 << 12) -> dict[str, 
     if wl.kv_dtype == "fp16":
         v["k_pool"] = normal16((NB, BLOCK, Hkv, D))
         v["v_pool"] = normal16((NB, BLOCK, Hkv, D))
+    elif wl.kv_dtype == "fp8":
+        for nm in ("k_pool", "v_pool"):
+            idx = torch.randint(0, 254, (NB, BLOCK, Hkv, D), generator=gen, device=dev,
+                                dtype=torch.int32)
+            # index -> code, skipping the NaN codes 0x7F and 0xFF
+            v[nm] = (idx + (idx >= 0x7F).to(torch.int32)).to(torch.uint8)
+        for nm in ("k_scale", "v_scale"):
+            t = torch.rand((NB, Hkv, BLOCK), generator=gen, device=dev, dtype=torch.float32)
+            v[nm] = t * (1.5 / 448) + (2.3 / 448)
     else:
         for nm in ("k_pool", "v_pool"):
             v[nm] = torch.randint(-127, 128, (NB, BLOCK, Hkv, D), generator=gen,
