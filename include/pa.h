@@ -138,6 +138,32 @@ int pa_write_kv_fp8(const void* k_new, const void* v_new, const int32_t* slot_ma
                     int head_dim, void* stream);
 
 /*
+ * Block copy for copy-on-write.  The zskr.cn article on ATB's PagedAttention
+ * (section "踩坑三") updates a page that several requests share by taking a
+ * fresh page, copying the old page into it and only then writing the new
+ * token; the caller's block manager decides which blocks to copy
+ * (reference counts, section "踩坑二"), this call copies them on the device.
+ *
+ *   k_pool, v_pool   the pools, [num_blocks, block_size, kv_heads, head_dim]
+ *                    of elem_bytes each (2: fp16; 1: int8 or fp8 codes)
+ *   k_scale, v_scale fp32 [num_blocks, kv_heads, block_size]; required when
+ *                    elem_bytes is 1 (copied with their blocks), ignored
+ *                    when it is 2
+ *   block_pairs      int32 [num_pairs][2] on the device: (src, dst) block
+ *                    ids; every element of block src (K, V and scales) is
+ *                    copied to block dst.  A pair naming a block outside
+ *                    [0, num_blocks) is skipped.  Caller contract: the dst
+ *                    blocks are distinct and none is also a src of the same
+ *                    call (the copies run concurrently).
+ * Returns PA_OK, PA_ERR_NULL, PA_ERR_SHAPE (negative counts, non-positive
+ * sizes) or PA_ERR_UNSUPPORTED (block_size != 16, head_dim not 64/128,
+ * elem_bytes not 1/2); num_pairs = 0 is a no-op.  Asynchronous on `stream`.
+ */
+int pa_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                   const int32_t* block_pairs, int num_pairs, int num_blocks, int block_size,
+                   int kv_heads, int head_dim, int elem_bytes, void* stream);
+
+/*
  * Partition size the library uses for these shapes when partition_size is
  * 0, else partition_size itself (a multiple of 16).  The library's choice:
  * 256 tokens, the finest split, with runs of partitions merged on the

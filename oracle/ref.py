@@ -309,3 +309,31 @@ def ref_quantize_fp8(x):
     codes = _nearest_e4m3(x32 / s)
     return codes, s[..., 0]
 
+
+
+def ref_copy_blocks(k_pool, v_pool, pairs, k_scale=None, v_scale=None):
+    """Copy-on-write block copy: for each (src, dst) pair, every slot of
+    block src (K, V and, for 8-bit pools, the scales) is copied to block
+    dst.  The zskr.cn article on ATB's PagedAttention ("踩坑三") takes a
+    fresh page for a shared page that is about to be written, copies the old
+    page into it and then writes.  Returns new arrays (scales None when not
+    given).  Out-of-range ids, a repeated dst, or a dst that is also a src
+    raise ValueError (the result would depend on the order of the copies)."""
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    ks_out = None if k_scale is None else np.array(k_scale, copy=True)
+    vs_out = None if v_scale is None else np.array(v_scale, copy=True)
+    pairs = [(int(a), int(b)) for a, b in np.asarray(pairs).reshape(-1, 2).tolist()]
+    nb = k_pool.shape[0]
+    dsts = [d for _, d in pairs]
+    if len(set(dsts)) != len(dsts) or set(dsts) & {s for s, _ in pairs}:
+        raise ValueError("copy pairs: dst blocks must be distinct and not sources")
+    for src, dst in pairs:
+        if not (0 <= src < nb and 0 <= dst < nb):
+            raise ValueError(f"block pair ({src}, {dst}) out of range")
+        k_out[dst] = k_pool[src]
+        v_out[dst] = v_pool[src]
+        if ks_out is not None:
+            ks_out[dst] = k_scale[src]
+            vs_out[dst] = v_scale[src]
+    return k_out, v_out, ks_out, vs_out

@@ -13,6 +13,7 @@ Functions mirror the C entry points:
   decode(q, k_pool, v_pool, block_table, context_lens, ...)
   decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, ...)
   decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, ...)
+  copy_blocks(k_pool, v_pool, block_pairs, k_scale=None, v_scale=None)
 
 FP8 pools hold raw OCP E4M3 codes: torch.uint8 tensors (a torch.float8_e4m3fn
 tensor is accepted and viewed as its bytes).
@@ -29,7 +30,7 @@ import os
 __all__ = [
     "PaError", "LIB_PATH", "lib", "status_string", "write_kv", "write_kv_int8",
     "write_kv_fp8", "partition_size", "workspace_size", "decode", "decode_int8",
-    "decode_fp8", "decode_partials",
+    "decode_fp8", "copy_blocks", "decode_partials",
     "decode_partials_int8", "merge_partials", "decode_shared_prefix",
     "shared_prefix_workspace_size", "EXPORTS",
 ]
@@ -47,7 +48,7 @@ import torch  # noqa: E402,F401
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libpa.so not found at {LIB_PATH}; build it with "
-        "`python -m paged_kv_cache_238_amd.build` (hipcc, gfx950)")
+        "`python paged_kv_cache_238_amd/build.py` (hipcc, gfx950)")
 lib = ctypes.CDLL(LIB_PATH)
 
 _p = ctypes.c_void_p
@@ -61,6 +62,7 @@ EXPORTS = {
     "pa_write_kv": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "pa_write_kv_int8": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "pa_write_kv_fp8": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
+    "pa_copy_blocks": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
     "pa_decode_partition_size": (_i, [_i, _i, _i, _i, _i, _i]),
     "pa_decode_workspace_size": (_z, [_i, _i, _i, _i, _i, _i]),
     "pa_decode": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i,
@@ -200,6 +202,31 @@ def write_kv_fp8(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale, v_scale) -
     the uint8 pools, with their fp32 scales, at slot slot_mapping[i]."""
     _write_q8(lib.pa_write_kv_fp8, "pa_write_kv_fp8", _torch().uint8, k_new, v_new,
               slot_mapping, _codes(k_pool), _codes(v_pool), k_scale, v_scale)
+
+
+def copy_blocks(k_pool, v_pool, block_pairs, k_scale=None, v_scale=None) -> None:
+    """Copy whole blocks src -> dst for each row (src, dst) of block_pairs
+    (int32 [n, 2] on the pools' device): K, V and, for 8-bit pools, their
+    scales.  dst blocks must be distinct and not also be a src."""
+    torch = _torch()
+    k_pool, v_pool = _codes(k_pool), _codes(v_pool)
+    dev = k_pool.device
+    q8 = k_pool.dtype in (torch.int8, torch.uint8)
+    _need(k_pool, "k_pool", k_pool.dtype if q8 else torch.float16, 4)
+    _need(v_pool, "v_pool", k_pool.dtype, 4, dev)
+    _need(block_pairs, "block_pairs", torch.int32, 2, dev)
+    NB, bs, Hkv, D = k_pool.shape
+    if v_pool.shape != k_pool.shape or block_pairs.shape[1:] != (2,):
+        raise ValueError("copy_blocks: inconsistent shapes")
+    if q8:
+        _need(k_scale, "k_scale", torch.float32, 3, dev)
+        _need(v_scale, "v_scale", torch.float32, 3, dev)
+        if k_scale.shape != (NB, Hkv, bs) or v_scale.shape != k_scale.shape:
+            raise ValueError("copy_blocks: scale shapes must be [num_blocks, kv_heads, block_size]")
+    _check(lib.pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(k_scale) if q8 else None,
+                              _ptr(v_scale) if q8 else None, _ptr(block_pairs),
+                              block_pairs.shape[0], NB, bs, Hkv, D, 1 if q8 else 2,
+                              _stream(k_pool)), "pa_copy_blocks")
 
 
 def partition_size(batch, q_heads, kv_heads, head_dim, max_context_len, partition_size=0) -> int:

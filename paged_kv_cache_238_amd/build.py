@@ -1,6 +1,6 @@
 """Build libpa.so for gfx950 in-tree with hipcc.
 
-    python -m paged_kv_cache_238_amd.build
+    python paged_kv_cache_238_amd/build.py
 
 Compiles every csrc/*.hip into one shared library next to this file.  All
 device code is built without packed-fp32 instructions.
@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.hip", "decode.hip", "decode_mfma.hip", "merge.hip", "write_kv.hip"]
+SOURCES = ["pa_api.hip", "decode.hip", "decode_mfma.hip", "merge.hip", "write_kv.hip",
+           "copy_blocks.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -384,6 +384,30 @@ int pa_write_kv_fp8(const void* k_new, const void* v_new, const int32_t* slot_ma
                   num_tokens, num_blocks, block_size, kv_heads, head_dim, stream);
 }
 
+int pa_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                   const int32_t* block_pairs, int num_pairs, int num_blocks, int block_size,
+                   int kv_heads, int head_dim, int elem_bytes, void* stream) {
+  if (!k_pool || !v_pool) return PA_ERR_NULL;
+  if (num_pairs < 0 || num_blocks <= 0 || kv_heads <= 0 || head_dim <= 0) return PA_ERR_SHAPE;
+  if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (elem_bytes != 1 && elem_bytes != 2) return PA_ERR_UNSUPPORTED;
+  if (elem_bytes == 1 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (num_pairs > 0 && !block_pairs) return PA_ERR_NULL;
+  if (num_pairs == 0) return PA_OK;
+  pa::CopyParams p = {};
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.k_scale = elem_bytes == 1 ? k_scale : nullptr;
+  p.v_scale = elem_bytes == 1 ? v_scale : nullptr;
+  p.pairs = block_pairs;
+  p.num_pairs = num_pairs;
+  p.num_blocks = num_blocks;
+  p.scales_per_block = kv_heads * kBlockTokens;
+  p.block_bytes = (size_t)kBlockTokens * kv_heads * head_dim * elem_bytes;
+  return status_of(pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)));
+}
+
 int pa_decode_partition_size(int batch, int q_heads, int kv_heads, int head_dim,
                              int max_context_len, int partition_size) {
   if (check_decode_shapes(1 << 30 >> 4, max_context_len, batch, q_heads, kv_heads, head_dim,

@@ -80,6 +80,17 @@ struct WriteParams {
   long long capacity;         // num_blocks * 16 slots
 };
 
+struct CopyParams {
+  void* k_pool;               // any element type; blocks are byte runs
+  void* v_pool;
+  float* k_scale;             // 8-bit pools: [NB, Hkv, 16]; null for fp16
+  float* v_scale;
+  const int32_t* pairs;       // [num_pairs][2]: (src block, dst block)
+  int num_pairs, num_blocks;
+  int scales_per_block;       // kv_heads * 16
+  size_t block_bytes;         // 16 * kv_heads * head_dim * element bytes
+};
+
 // Workgroups of a decode launch with `wpg` kv heads per workgroup: one per
 // sequence in direct mode; otherwise the number of (run, head group)
 // items, bounded on the host (locate_run in run_span.h): at most
@@ -106,5 +117,6 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_write_kv(const WriteParams& p, hipStream_t stream);
 hipError_t launch_write_kv_int8(const WriteParams& p, hipStream_t stream);
 hipError_t launch_write_kv_fp8(const WriteParams& p, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
 
 }  // namespace pa
