@@ -10,10 +10,13 @@
 // across partitions instead of token by token, followed by that kernel's
 // final normalisation and fp16 store.
 //
-// One workgroup of 256 lanes per (sequence, query head): lanes are split
-// into D/4 float4 columns x (1024/D) partition phases; each lane sums its
-// phase's partitions, then the phases are added through LDS in a fixed
-// order (deterministic).
+// Rows with at most 32 records (the partition count bounds them): one wave
+// per (sequence, query head), four rows per workgroup; lanes are D/4 float4
+// columns x 256/D record phases, every record a lane needs is loaded at
+// once (one memory round trip), and the phases are added by shuffles in a
+// fixed order.  Longer rows: one workgroup of 256 lanes per row, D/4
+// columns x 1024/D phases, phases added through LDS in a fixed order.  Both
+// are deterministic.
 //
 // Shared-prefix decode merges two record sets per row: the runs over the
 // private suffix [prefix, L) and n_pre records over the shared prefix;
@@ -24,8 +27,21 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kHeld = 8;        // records per lane held in registers (one round trip)
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.693147180559945309f;
+
+// Maximum over the workgroup, through LDS; every lane gets it.
+__device__ __forceinline__ float block_max(float x, float* s_max) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = s_max[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) x = fmaxf(x, s_max[i]);
+  return x;
+}
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   _Float16 h = (_Float16)x;
@@ -70,29 +86,53 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
     return i < n_suf ? o[(size_t)i * COLS + col] : o2[(size_t)(i - n_suf) * COLS + col];
   };
 
-  // M = max_p m_p
-  float M = kNegInf;
-  for (int i = tid; i < n; i += kThreads) M = fmaxf(M, rec_ml(i).x);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if ((tid & 63) == 0) s_max[tid >> 6] = M;
-  __syncthreads();
-  M = s_max[0];
-#pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) M = fmaxf(M, s_max[i]);
-  const float Mu = (M == kNegInf) ? 0.f : M;
-
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.f;
-  for (int i = ph; i < n; i += PH) {
-    const float2 r = rec_ml(i);
-    const float wgt = __builtin_amdgcn_exp2f(r.x - Mu);
-    den = fmaf(wgt, r.y, den);
-    const float4 v = rec_o(i);
-    acc.x = fmaf(wgt, v.x, acc.x);
-    acc.y = fmaf(wgt, v.y, acc.y);
-    acc.z = fmaf(wgt, v.z, acc.z);
-    acc.w = fmaf(wgt, v.w, acc.w);
+  float M = kNegInf;
+  if (n <= PH * kHeld) {
+    // Every record this lane needs (phase ph: records ph, ph + PH, ...) is
+    // loaded at once, so the whole merge costs one memory round trip.
+    float2 r[kHeld];
+    float4 v[kHeld];
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) {
+      const int i = ph + k * PH;
+      r[k] = make_float2(kNegInf, 0.f);
+      v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < n) {
+        r[k] = rec_ml(i);
+        v[k] = rec_o(i);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) M = fmaxf(M, r[k].x);
+    M = block_max(M, s_max);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) {
+      if (ph + k * PH < n) {
+        const float wgt = __builtin_amdgcn_exp2f(r[k].x - Mu);
+        den = fmaf(wgt, r[k].y, den);
+        acc.x = fmaf(wgt, v[k].x, acc.x);
+        acc.y = fmaf(wgt, v[k].y, acc.y);
+        acc.z = fmaf(wgt, v[k].z, acc.z);
+        acc.w = fmaf(wgt, v[k].w, acc.w);
+      }
+    }
+  } else {
+    for (int i = tid; i < n; i += kThreads) M = fmaxf(M, rec_ml(i).x);
+    M = block_max(M, s_max);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    for (int i = ph; i < n; i += PH) {
+      const float2 r = rec_ml(i);
+      const float wgt = __builtin_amdgcn_exp2f(r.x - Mu);
+      den = fmaf(wgt, r.y, den);
+      const float4 v = rec_o(i);
+      acc.x = fmaf(wgt, v.x, acc.x);
+      acc.y = fmaf(wgt, v.y, acc.y);
+      acc.z = fmaf(wgt, v.z, acc.z);
+      acc.w = fmaf(wgt, v.w, acc.w);
+    }
   }
   s_acc[ph][col] = acc;
   if (col == 0) s_den[ph] = den;
@@ -118,17 +158,110 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   }
 }
 
+constexpr int kWaveHeld = 16;   // records per lane in the wave-per-row kernel
+constexpr int kRowsPerGroup = kThreads / 64;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_wave_kernel(const MergeParams p) {
+  constexpr int COLS = D / 4;              // float4 columns
+  constexpr int PH = 64 / COLS;            // record phases within the wave
+  const int lane = threadIdx.x & 63, col = lane % COLS, ph = lane / COLS;
+  const long long rowid = (long long)blockIdx.x * kRowsPerGroup + (threadIdx.x >> 6);
+  if (rowid >= (long long)p.batch * p.q_heads) return;
+  const int b = (int)(rowid / p.q_heads);
+  const size_t row = (size_t)rowid;
+  const int L = p.context_lens[b] - p.token_offset;
+  if (L < 0 || L > p.max_context_len) {
+    for (int d = lane; d < D; d += 64) p.out[row * D + d] = 0x7E00;
+    if (lane == 0 && p.lse) p.lse[row] = __builtin_nanf("");
+    return;
+  }
+  const int span = max(1, p.header[0]);
+  const int n_part_b = (L + p.partition_size - 1) / p.partition_size;
+  const int n_suf = (n_part_b + span - 1) / span;
+  const int n_pre = p.pre_ml ? p.n_pre : 0;
+  const int n = n_suf + n_pre;
+  if (n == 0) {
+    for (int d = lane; d < D; d += 64) p.out[row * D + d] = 0;
+    if (lane == 0 && p.lse) p.lse[row] = kNegInf;
+    return;
+  }
+  const float2* ml = p.part_ml + row * p.n_part;
+  const float4* o = reinterpret_cast<const float4*>(p.part_o + row * p.n_part * D);
+  const float2* ml2 = n_pre ? p.pre_ml + row * n_pre : nullptr;
+  const float4* o2 = n_pre ? reinterpret_cast<const float4*>(p.pre_o + row * n_pre * D) : nullptr;
+  float2 r[kWaveHeld];
+  float4 v[kWaveHeld];
+#pragma unroll
+  for (int k = 0; k < kWaveHeld; ++k) {
+    const int i = ph + k * PH;
+    r[k] = make_float2(kNegInf, 0.f);
+    v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < n) {
+      r[k] = i < n_suf ? ml[i] : ml2[i - n_suf];
+      v[k] = i < n_suf ? o[(size_t)i * COLS + col] : o2[(size_t)(i - n_suf) * COLS + col];
+    }
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int k = 0; k < kWaveHeld; ++k) M = fmaxf(M, r[k].x);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+#pragma unroll
+  for (int k = 0; k < kWaveHeld; ++k) {
+    if (ph + k * PH < n) {
+      const float wgt = __builtin_amdgcn_exp2f(r[k].x - Mu);
+      den = fmaf(wgt, r[k].y, den);
+      acc.x = fmaf(wgt, v[k].x, acc.x);
+      acc.y = fmaf(wgt, v[k].y, acc.y);
+      acc.z = fmaf(wgt, v[k].z, acc.z);
+      acc.w = fmaf(wgt, v[k].w, acc.w);
+    }
+  }
+  // phases in order: lane col of phase q holds its partial sums
+  float dsum = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int q = 0; q < PH; ++q) {
+    const int src = col + q * COLS;
+    dsum += __shfl(den, src);
+    a.x += __shfl(acc.x, src);
+    a.y += __shfl(acc.y, src);
+    a.z += __shfl(acc.z, src);
+    a.w += __shfl(acc.w, src);
+  }
+  if (ph == 0) {
+    uint16_t* dst = p.out + row * D + col * 4;
+    dst[0] = f32_to_f16_bits(a.x / dsum);
+    dst[1] = f32_to_f16_bits(a.y / dsum);
+    dst[2] = f32_to_f16_bits(a.z / dsum);
+    dst[3] = f32_to_f16_bits(a.w / dsum);
+    if (col == 0 && p.lse) p.lse[row] = (M + log2f(dsum)) * kLn2;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const MergeParams& p, hipStream_t stream) {
+  // records per row are at most n_part (+ the prefix records)
+  if (p.n_part + (p.pre_ml ? p.n_pre : 0) <= kWaveHeld * (256 / D)) {
+    const long long rows = (long long)p.batch * p.q_heads;
+    const unsigned groups = (unsigned)((rows + kRowsPerGroup - 1) / kRowsPerGroup);
+    hipLaunchKernelGGL(merge_wave_kernel<D>, dim3(groups), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(merge_kernel<D>, dim3(p.q_heads, p.batch), dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
-  dim3 grid(p.q_heads, p.batch);
-  if (p.head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kThreads), 0, stream, p);
-  else if (p.head_dim == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kThreads), 0, stream, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (p.head_dim == 128) return launch_d<128>(p, stream);
+  if (p.head_dim == 64) return launch_d<64>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa
