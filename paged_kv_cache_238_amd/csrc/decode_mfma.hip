@@ -44,6 +44,8 @@ typedef short s4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;   // at most eight waves (kv heads) per workgroup
+// Block ids of a run staged in LDS per workgroup, refilled kIdCap at a time.
+constexpr int kIdCap = 1024;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.693147180559945309f;
 #ifndef PA_V_ROW_PAD
@@ -68,6 +70,26 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr int kLongContext = 32768;   // tokens; see waves_per_group
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reductions over the four lane groups l, l^16, l^32, l^48 (the lanes that
+// share a query slot).  gfx950's permlane swaps trade row halves between two
+// registers on the VALU, without the LDS round trip of a lane shuffle: with
+// both operands equal to x, the swapped pair holds x[l] and x[l ^ 32] (then
+// x[l ^ 16]) in every lane, each pair ordered low lane first, so both lanes
+// of a pair compute the same value.
+__device__ __forceinline__ float group_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float group_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   _Float16 h = (_Float16)x;
@@ -130,24 +152,44 @@ __device__ __forceinline__ void f8x16_to_h16(const uint4& c, uint4& first, uint4
   f8x4_to_h4(c.w, second.z, second.w);
 }
 
+// Which bytes of a block each lane loads, and which head-dim elements it then
+// feeds to the QK product: load ld has lane (li, g) read bytes 64 ld + 16 g
+// .. + 15 of its head's row in token li, so each load covers 64 bytes of all
+// 16 rows and lane (li, g) holds row li, as the A operand wants.  (Loads of
+// whole 128-byte lines, 8 rows per instruction, with a DPP exchange between
+// lanes l and l ^ 8 to restore the operand layout, measured 1-2 % slower:
+// the exchange costs more than the wider lines save.)
 template <int D, bool I8>
 struct Geometry {
+  static constexpr int kEsz = I8 ? 1 : 2;
   // 16-byte global loads per lane per block for K (and again for V).
-  static constexpr int kLoads = I8 ? D / 64 : D / 32;
-  // QK MFMA steps (8 dims of k per lane each).
+  static constexpr int kLoads = D * kEsz / 64;
+  // QK MFMA steps (8 elements of k per lane each).
   static constexpr int kSteps = D / 32;
-  // Head-dim index held by lane group g, element j of QK step kk.
+  // Head-dim element held by lane group g, element j of QK step kk.
   static __device__ __forceinline__ int dim(int kk, int g, int j) {
     if constexpr (I8) return 64 * (kk / 2) + 16 * g + 8 * (kk % 2) + j;
     else return 32 * kk + 8 * g + j;
   }
-  // Byte offset, within a token row of D elements, of load `ld` of group g.
-  static __device__ __forceinline__ uint32_t load_off(int ld, int g) {
-    if constexpr (I8) return (uint32_t)(64 * ld + 16 * g);
-    else return (uint32_t)(64 * ld + 16 * g);   // 32*ld + 8*g elements of 2 bytes
+  // Token row (0..15) and byte offset within the head's row of load ld.
+  static __device__ __forceinline__ int load_row(int ld, int lane) { return lane & 15; }
+  static __device__ __forceinline__ int load_col(int ld, int lane) {
+    return 64 * ld + 16 * (lane >> 4);
   }
   static constexpr int kRowBytes = D * 2 + kRowPad;   // LDS row of the fp16 V tile
 };
+
+// Scale of token 4 lg + i from a register holding, at row position p, the
+// scale of token (p + 4 lg) % 16: broadcast of row position i (DPP
+// row_newbcast, no memory access).
+__device__ __forceinline__ float scale_of(float x, int i) {
+  switch (i) {
+    case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x151, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x152, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x153, 0xF, 0xF, false));
+  }
+}
 
 // Three waves per SIMD (<= 168 registers) with two (fp16) or three (int8)
 // register sets of block loads; deeper rotation at two waves per SIMD and
@@ -218,22 +260,14 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int32_t* bt_row =
       p.block_table + (size_t)b * p.bt_stride + p.token_offset / kBlockTokens;
 
-  // Start-up loads, all independent: the length, the first 64 block ids of
-  // the run (clamped to the table row; only those below the length are
-  // used) and Q.  Block ids live one per lane and are read back with
-  // v_readlane, so the table slice is fetched once per wave.
+  // Start-up loads, all independent: the length and Q.
   const int L = PREFIX ? p.max_context_len : p.context_lens[b] - p.token_offset;
   const int row_left = p.max_blocks - j0;
   const int span_blocks = span * (P / kBlockTokens);
-  // Block ids c0 .. c0+63 of the run, one per lane, through a buffer
-  // resource bounded to the run's slice of the table row: ids past the
-  // slice read as 0 with no branch, so the load stays asynchronous.
+  // The run's slice of the table row as a buffer resource: ids past the
+  // slice read as 0 with no branch.
   const __amdgpu_buffer_rsrc_t rids =
       make_rsrc(bt_row + j0, (uint32_t)max(min(span_blocks, row_left), 0) * 4u);
-  auto load_ids = [&](int c0) {
-    return (int)__builtin_amdgcn_raw_buffer_load_b32(rids, (uint32_t)(c0 + lane) * 4u, 0, 0);
-  };
-  int ids = load_ids(0);
 
   // Q^T as the B operand of the QK product: lane holds Q[slot li][dim(kk, lg, j)].
   // Each step's 8 dims are consecutive (Geo::dim), so one 16-byte load each;
@@ -270,6 +304,17 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int tail = ntok - nfull * kBlockTokens;
 
   char* s_tile = smem + w * TILE;            // this wave's V tile
+  // Block ids of the run, shared by the workgroup (all its waves stream the
+  // same run, so every step below is taken by all of them together).  Ids
+  // come from LDS in order, each read NBUF blocks before its block is
+  // issued, so no block waits on a table read.
+  int32_t* s_ids = reinterpret_cast<int32_t*>(smem + wpg * TILE);
+  auto fill_ids = [&](int base) {            // ids base .. base + kIdCap - 1
+    __syncthreads();                         // the previous chunk is read
+    for (int t = tid; t < kIdCap; t += blockDim.x)
+      s_ids[t] = (int)__builtin_amdgcn_raw_buffer_load_b32(rids, (uint32_t)(base + t) * 4u, 0, 0);
+    __syncthreads();
+  };
 
   // int8: sum over head_dim of q for head li (removes the 1152 bias of K).
   float qbias = 0.f;
@@ -279,8 +324,7 @@ void decode_mfma_kernel(const DecodeParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) qbias += (float)qB[kk][j];
     }
-    qbias += __shfl_xor(qbias, 16);
-    qbias += __shfl_xor(qbias, 32);
+    qbias = group_sum(qbias);
     qbias *= 1152.0f;
   }
 
@@ -293,7 +337,17 @@ void decode_mfma_kernel(const DecodeParams p) {
 
   const uint32_t row_bytes = (uint32_t)Hkv * D * ESZ;          // one token row, all heads
   const uint32_t blk_bytes = (uint32_t)kBlockTokens * row_bytes;
-  const uint32_t lane_row_off = (uint32_t)li * row_bytes + (uint32_t)g * D * ESZ;
+  // Offsets of this lane's loads within a block, and their V tile targets.
+  uint32_t ld_off[NLD];
+  uint32_t ld_lds[NLD];
+  int ld_row[NLD];
+#pragma unroll
+  for (int ld = 0; ld < NLD; ++ld) {
+    ld_row[ld] = Geo::load_row(ld, lane);
+    const int col = Geo::load_col(ld, lane);
+    ld_off[ld] = (uint32_t)ld_row[ld] * row_bytes + (uint32_t)g * D * ESZ + (uint32_t)col;
+    ld_lds[ld] = (uint32_t)ld_row[ld] * Geo::kRowBytes + (uint32_t)(col / ESZ) * 2;
+  }
   const char* kbase = static_cast<const char*>(p.k_pool);
   const char* vbase = static_cast<const char*>(p.v_pool);
   const uint32_t scale_blk_bytes = (uint32_t)kBlockTokens * Hkv * sizeof(float);
@@ -305,8 +359,8 @@ void decode_mfma_kernel(const DecodeParams p) {
   struct Regs {
     uint4 k[NLD];
     uint4 v[NLD];
-    f4 ks;          // int8: scales of this lane's softmax tokens 4*lg .. 4*lg+3
-    f4 vs;
+    float ks;       // 8-bit: scale of token (li + 4 lg) % 16 (rotated; see scale_of)
+    float vs;
   };
 
   // Loads of one block.  real == false: a prefetch past the end; its
@@ -321,17 +375,22 @@ void decode_mfma_kernel(const DecodeParams p) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)blk * blk_bytes, nbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)blk * blk_bytes, nbytes);
 #pragma unroll
-    for (int ld = 0; ld < NLD; ++ld) R.k[ld] = buffer_load16(rk, lane_row_off + Geo::load_off(ld, lg));
+    for (int ld = 0; ld < NLD; ++ld) R.k[ld] = buffer_load16(rk, ld_off[ld]);
 #pragma unroll
-    for (int ld = 0; ld < NLD; ++ld) R.v[ld] = buffer_load16(rv, lane_row_off + Geo::load_off(ld, lg));
+    for (int ld = 0; ld < NLD; ++ld) R.v[ld] = buffer_load16(rv, ld_off[ld]);
     if constexpr (I8) {
-      // scales [NB, Hkv, 16]: this lane's four softmax tokens 4*lg .. 4*lg+3
-      // of kv head g are one 16-byte load
+      // scales [NB, Hkv, 16] of kv head g: one float per lane, rotated by
+      // 4 lg within each row of 16 lanes so that the four tokens 4 lg .. 4 lg+3
+      // of this lane's softmax slots sit at row positions 0..3 (scale_of).
+      // Four bytes per lane: a 16-byte load per lane of the same 64 bytes
+      // costs the vector memory path four times the lane data.
       const uint32_t sbytes = real ? scale_blk_bytes : 0u;
       const size_t sblk = (size_t)blk * kBlockTokens * Hkv;
-      const uint32_t soff = ((uint32_t)g * kBlockTokens + 4 * lg) * 4u;
-      R.ks = __builtin_bit_cast(f4, buffer_load16(make_rsrc(p.k_scale + sblk, sbytes), soff));
-      R.vs = __builtin_bit_cast(f4, buffer_load16(make_rsrc(p.v_scale + sblk, sbytes), soff));
+      const uint32_t soff = ((uint32_t)g * kBlockTokens + (uint32_t)((li + 4 * lg) & 15)) * 4u;
+      R.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           make_rsrc(p.k_scale + sblk, sbytes), soff, 0, 0));
+      R.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           make_rsrc(p.v_scale + sblk, sbytes), soff, 0, 0));
     }
   };
   auto process_block = [&](auto tail_tag, const Regs& R, int valid) {
@@ -356,29 +415,23 @@ void decode_mfma_kernel(const DecodeParams p) {
     for (int kk = 0; kk < NKK; ++kk)
       s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qB[kk], s, 0, 0, 0);
 
-    // V into this wave's LDS tile, natural [token][dim] order (fp16).
-    {
-      const bool zero_row = TAIL && li >= valid;   // tail slot: may hold NaN
-      char* rowp = s_tile + li * Geo::kRowBytes;
+    // V into this wave's LDS tile, natural [token][dim] order (fp16); a
+    // tail row past `valid` may hold NaN and is zeroed.
+#pragma unroll
+    for (int ld = 0; ld < NLD; ++ld) {
+      const bool zero_row = TAIL && ld_row[ld] >= valid;
+      char* dst = s_tile + ld_lds[ld];
       if constexpr (I8) {
-#pragma unroll
-        for (int ld = 0; ld < NLD; ++ld) {
-          uint4 a, c;
-          if constexpr (KV == kKvI8) i8x16_to_h16(R.v[ld], a, c);
-          else f8x16_to_h16(R.v[ld], a, c);
-          if (zero_row) a = c = make_uint4(0, 0, 0, 0);
-          const int d0 = 64 * ld + 16 * lg;
-          *reinterpret_cast<uint4*>(rowp + d0 * 2) = a;
-          *reinterpret_cast<uint4*>(rowp + d0 * 2 + 16) = c;
-        }
+        uint4 a, c;
+        if constexpr (KV == kKvI8) i8x16_to_h16(R.v[ld], a, c);
+        else f8x16_to_h16(R.v[ld], a, c);
+        if (zero_row) a = c = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(dst) = a;
+        *reinterpret_cast<uint4*>(dst + 16) = c;
       } else {
-#pragma unroll
-        for (int ld = 0; ld < NLD; ++ld) {
-          uint4 a = R.v[ld];
-          if (zero_row) a = make_uint4(0, 0, 0, 0);
-          const int d0 = 32 * ld + 8 * lg;
-          *reinterpret_cast<uint4*>(rowp + d0 * 2) = a;
-        }
+        uint4 a = R.v[ld];
+        if (zero_row) a = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(dst) = a;
       }
     }
 
@@ -387,7 +440,7 @@ void decode_mfma_kernel(const DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float x;
-      if constexpr (I8) x = (s[i] - qbias) * (p.scale_log2 * R.ks[i]);
+      if constexpr (I8) x = (s[i] - qbias) * (p.scale_log2 * scale_of(R.ks, i));
       else x = s[i] * p.scale_log2;
       if constexpr (TAIL) {
         if (4 * lg + i >= valid) x = kNegInf;
@@ -395,8 +448,7 @@ void decode_mfma_kernel(const DecodeParams p) {
       sc[i] = x;
     }
     float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    mb = group_max(mb);
     // Move the reference max only when some head of the wave outgrows it.
     if (__builtin_amdgcn_ballot_w64(mb > m_run + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_run, mb);
@@ -416,7 +468,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     for (int i = 0; i < 4; ++i) {
       float pv = pr[i];
       if constexpr (I8) {
-        float vsc = R.vs[i];
+        float vsc = scale_of(R.vs, i);
         if constexpr (TAIL) {
           if (4 * lg + i >= valid) vsc = 0.f;
         }
@@ -441,8 +493,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   // Lane (lg, li) holds O[head li][dim 16n + 4lg + i].
   auto finalize = [&]() {
     float den = l_run;
-    den += __shfl_xor(den, 16);
-    den += __shfl_xor(den, 32);
+    den = group_sum(den);
     if (qrow >= 0) {
       const size_t row = (size_t)qrow;
       float M = m_run;
@@ -473,51 +524,54 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
   };
 
-  // Full blocks of the run, streamed in order.  Block ids come one per lane
-  // from `ids`, a 64-block chunk; the following chunk is fetched into
-  // `ids_next` a whole chunk ahead and moved over just before its first
-  // block is issued, so no issue reads a register whose load may still be
-  // pending.  Register sets rotate so that NBUF - 1 blocks are in flight
-  // while one is reduced (int8 blocks are half the bytes, so they go one
-  // deeper); prefetches past the end read nothing.  Every branch is
-  // wave-uniform and no load sits inside one, so the waits stay exact.
+  // Full blocks of the run, streamed in order.  Register sets rotate so that
+  // NBUF - 1 blocks are in flight while one is reduced (int8 blocks are half
+  // the bytes, so they go one deeper); prefetches past the end read nothing.
+  // Block ids: each register set carries nid, the id of the next block it
+  // will receive, read from LDS when its current block is issued.  Every
+  // branch is wave-uniform (workgroup-uniform where it holds a barrier) and
+  // no vector load sits inside one, so the waits stay exact.
   constexpr int NBUF = I8 ? PA_MFMA_NBUF_I8 : PA_MFMA_NBUF_F16;
   std::integral_constant<bool, false> full;
-  // The chunk of the partial last block is moved in too, so its id is in `ids`.
-  const int nreal = nfull + (tail > 0 ? 1 : 0);
-  int ids_next = load_ids(64);
-  int next_chunk = 1;                        // chunk held in `ids_next`
-  auto issue = [&](int k, Regs& R) {
-    const bool real = k < nfull;
-    load_block(__builtin_amdgcn_readlane(ids, real ? (k & 63) : 0), real, R);
-  };
-  auto done = [&](int k) {                   // block k reduced; k + NBUF is issued next
-    if (((k + NBUF) & 63) == 0 && k + NBUF < nreal) {
-      ids = ids_next;
-      ++next_chunk;
-      ids_next = load_ids(next_chunk * 64);
-    }
-  };
+  // Id of the partial last block, in flight while the full blocks stream.
+  const int tail_id = (int)__builtin_amdgcn_raw_buffer_load_b32(rids, (uint32_t)nfull * 4u, 0, 0);
   if (nfull > 0) {
+    fill_ids(0);
+    int id_base = 0;                         // id held in s_ids[0]
+    auto lds_id = [&](int j) { return s_ids[min(j - id_base, kIdCap - 1)]; };
     Regs R[NBUF];
+    int nid[NBUF];
+    auto issue = [&](int j, int slot, int blk) {
+      load_block(blk, j < nfull, R[slot]);
+      if (j + NBUF - id_base >= kIdCap && j + NBUF < nfull) {
+        fill_ids(j + NBUF);                  // rare: runs longer than kIdCap blocks
+        id_base = j + NBUF;
+      }
+      nid[slot] = lds_id(j + NBUF);
+    };
+    // The prologue's loads stay in block order, so each block's wait
+    // counts only the blocks issued after it.
 #pragma unroll
-    for (int s = 0; s + 1 < NBUF; ++s) issue(s, R[s]);
+    for (int s = 0; s + 1 < NBUF; ++s) {
+      issue(s, s, __builtin_amdgcn_readfirstlane(lds_id(s)));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    nid[NBUF - 1] = lds_id(NBUF - 1);
     for (int k = 0; k < nfull; k += NBUF) {
 #pragma unroll
       for (int s = 0; s < NBUF; ++s) {
-        issue(k + s + NBUF - 1, R[(s + NBUF - 1) % NBUF]);
+        constexpr int kLast = NBUF - 1;
+        const int slot = (s + kLast) % NBUF;
+        issue(k + s + kLast, slot, __builtin_amdgcn_readfirstlane(nid[slot]));
         __builtin_amdgcn_sched_barrier(0);
-        if (s == 0 || k + s < nfull) {
-          process_block(full, R[s], kBlockTokens);
-          done(k + s);
-        }
+        if (s == 0 || k + s < nfull) process_block(full, R[s], kBlockTokens);
       }
     }
   }
   // The partial last block (only in a sequence's last run).
   if (tail > 0) {
     Regs T;
-    load_block(__builtin_amdgcn_readlane(ids, nfull & 63), true, T);
+    load_block(__builtin_amdgcn_readfirstlane(tail_id), true, T);
     process_block(std::integral_constant<bool, true>(), T, tail);
   }
   finalize();
@@ -536,7 +590,7 @@ template <int D, int G, int KV>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   using Geo = Geometry<D, KV != kKvF16>;
   const int wpg = waves_per_group(p);
-  const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes;
+  const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes + kIdCap * sizeof(int32_t);
   const unsigned grid = decode_workgroups(p, wpg);
   hipLaunchKernelGGL((decode_mfma_kernel<D, G, KV, false>), dim3(grid), dim3(64 * wpg), lds,
                      stream, p);
@@ -549,7 +603,7 @@ template <int D, int KV>
 hipError_t launch_prefix(const DecodeParams& p, hipStream_t stream) {
   using Geo = Geometry<D, KV != kKvF16>;
   const int wpg = (p.kv_heads % 4 == 0) ? 4 : (p.kv_heads % 2 == 0) ? 2 : 1;
-  const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes;
+  const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes + kIdCap * sizeof(int32_t);
   const unsigned grid = (unsigned)((long long)p.prefix_tiles * p.n_part * (p.kv_heads / wpg));
   hipLaunchKernelGGL((decode_mfma_kernel<D, 16, KV, true>), dim3(grid), dim3(64 * wpg), lds,
                      stream, p);

@@ -12,6 +12,7 @@
 // items(s) does not grow with s, so it is found by bisection.  Long
 // sequences therefore get long runs, and a batch of short or mixed lengths
 // keeps span 1.  When batch * kv_heads alone reaches the target, span is 1
+// and items map to (partition, sequence) directly, without reading lengths
 // (the library then normally picks one partition per sequence instead).
 //
 // Items are (run, head group) pairs over the real runs only, numbered
@@ -37,10 +38,44 @@ struct RunSlot {
   int grp;    // head group (kv heads grp*wpg .. grp*wpg+wpg-1)
 };
 
+// Cross-lane steps on the VALU (DPP and gfx950's permlane swaps) rather
+// than LDS lane shuffles: the run search is on every workgroup's start-up
+// path, where each shuffle's LDS round trip would add to the latency.
+__device__ inline int dpp(int x, int ctrl) {
+  switch (ctrl) {   // the control must be a constant
+    case 0xB1: return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true);    // quad lanes ^1
+    case 0x4E: return __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true);    // quad lanes ^2
+    case 0x124: return __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, true);  // row rotate 4
+    case 0x128: return __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, true);  // row rotate 8
+    case 0x111: return __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row shift 1
+    case 0x112: return __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row shift 2
+    case 0x114: return __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row shift 4
+    default: return __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);     // row shift 8
+  }
+}
+
+// Sum over the wave, wave-uniform result.
 __device__ inline int wave_sum(int x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return __builtin_amdgcn_readfirstlane(x);
+  x += dpp(x, 0xB1);
+  x += dpp(x, 0x4E);                         // every lane: its quad's sum
+  x += dpp(x, 0x124);
+  x += dpp(x, 0x128);                        // its row of 16
+  const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  x = (int)(a[0] + a[1]);                    // rows 0+1, 2+3
+  const auto c = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return __builtin_amdgcn_readfirstlane((int)(c[0] + c[1]));
+}
+
+// Inclusive prefix sum over the lanes (lane i: x_0 + ... + x_i).
+__device__ inline int wave_scan(int x) {
+  x += dpp(x, 0x111);
+  x += dpp(x, 0x112);
+  x += dpp(x, 0x114);
+  x += dpp(x, 0x118);                        // within each row of 16
+  // last lane of row 0 (2) into row 1 (3), then of row 1 into rows 2 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+  return x;
 }
 
 // Item of this workgroup.  Must be called by all 64 lanes of each wave; the
@@ -52,6 +87,15 @@ __device__ inline RunSlot locate_run(const DecodeParams& p, int groups) {
   const int item = blockIdx.x / groups;      // run number, head groups fastest
   if (p.direct) {
     if (item < p.batch) r.b = item;
+    return r;
+  }
+  if ((long long)p.batch * p.kv_heads >= p.target_waves) {
+    // Pairs alone fill the GPU: one partition per run, numbered partition
+    // index first (the host launches n_part * batch items); a workgroup
+    // whose sequence has no such partition finds an empty run and exits.
+    // No lengths are scanned, so the prologue does not grow with the batch.
+    r.ridx = item / p.batch;
+    r.b = item % p.batch;
     return r;
   }
   const int lane = threadIdx.x & 63;
@@ -73,7 +117,7 @@ __device__ inline RunSlot locate_run(const DecodeParams& p, int groups) {
     return runs * p.kv_heads;
   };
   int span = 1;
-  if ((long long)p.batch * p.kv_heads < p.target_waves && items(1) > p.target_waves) {
+  if (items(1) > p.target_waves) {
     int lo = 1, hi = max_part;               // items(lo) > target >= items(hi)
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -88,12 +132,7 @@ __device__ inline RunSlot locate_run(const DecodeParams& p, int groups) {
   int base = 0;                              // runs of the sequences before chunk b0
   for (int b0 = 0; b0 < p.batch; b0 += 64) {
     const int runs = runs_of(b0);
-    int incl = runs;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
+    const int incl = wave_scan(runs);
     const int chunk = __builtin_amdgcn_readlane(incl, 63);
     if (item < base + chunk) {
       // lanes whose runs all lie before the item form a prefix; the next

@@ -480,3 +480,48 @@ def test_runs_enumerated_over_many_sequences(pa, G, int8):
         assert not out[~live].any() and np.all(np.isneginf(lse[~live]))
         check_close(out[live], want[live], f"many sequences G={G} int8={int8} P={P}")
         np.testing.assert_allclose(lse[live], want_lse[live], rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("G,kv", [(1, "fp16"), (2, "int8"), (8, "fp16"), (8, "fp8")])
+def test_pairs_filling_the_gpu_split(pa, G, kv):
+    """batch * kv_heads above the wave target with a partition forced below
+    the longest context: every (partition, sequence) item is launched, items
+    past a sequence's end or of an empty or broken sequence leave no record,
+    and the merge sees only the real ones."""
+    over = dict(batch=1040, q_heads=G * 2, kv_heads=2, head_dim=64, lmin=1, lmax=900,
+                occupancy=0.9, kv_dtype=kv)
+    wl = gen.make("gqa70b_mixed", seed=900 + G + len(kv), overrides=over)
+    wl.context_lens[[3, 500, 1039]] = 0
+    wl.context_lens[[4, 777]] = [1, 900]
+    wl = _rebuild_table(wl)
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    d = device_inputs(wl, vals)
+    want, want_lse = oracle_decode(wl, vals)
+    live = wl.context_lens > 0
+    for P in (256, 16):
+        say(f"pairs fill GPU G={G} kv={kv} P={P} B={wl.batch}")
+        out, lse = gpu_decode(pa, wl, d, partition_size=P)
+        out, lse = out.cpu().numpy(), lse.cpu().numpy()
+        assert not out[~live].any() and np.all(np.isneginf(lse[~live]))
+        check_close(out[live], want[live], f"pairs fill GPU G={G} kv={kv} P={P}")
+        np.testing.assert_allclose(lse[live], want_lse[live], rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("G,kv", [(1, "fp16"), (2, "int8"), (8, "fp16"), (8, "int8"), (8, "fp8")])
+def test_large_logits(pa, G, kv):
+    """Q scaled by 12: scores spread over tens of log2 units inside a block,
+    so a running max that missed any lane group would overflow the fp16
+    probabilities (exp2 of more than 16) instead of matching the oracle."""
+    over = dict(batch=6, q_heads=G * 2, kv_heads=2, head_dim=128, lmin=20, lmax=2000,
+                occupancy=0.9, kv_dtype=kv)
+    wl = gen.make("gqa70b_mixed", seed=1200 + G + len(kv), overrides=over)
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    vals["q"] = (vals["q"].astype(np.float32) * 12).astype(np.float16)
+    d = device_inputs(wl, vals)
+    want, want_lse = oracle_decode(wl, vals)
+    assert np.abs(want_lse).max() > 20
+    for P in (0, 256):
+        say(f"large logits G={G} kv={kv} P={P}")
+        out, lse = gpu_decode(pa, wl, d, partition_size=P)
+        check_close(out.cpu().numpy(), want, f"large logits G={G} kv={kv} P={P}")
+        np.testing.assert_allclose(lse.cpu().numpy(), want_lse, rtol=0, atol=1e-3)
