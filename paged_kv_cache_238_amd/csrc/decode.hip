@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   const int Hq = p.q_heads, Hkv = p.kv_heads;
 
   // Workgroup item = (run, head group), assigned on the device over the
-  // real runs only, in contiguous shares per XCD (locate_run).
+  // real runs only, numbered sequence by sequence (locate_run).
   const int groups = Hkv / wpg;
   const RunSlot rs = locate_run(p, groups);
   const int span = rs.span;

@@ -220,7 +220,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int Hq = p.q_heads, Hkv = p.kv_heads;
 
   // Workgroup item = (run, head group), assigned on the device over the
-  // real runs only, in contiguous shares per XCD (locate_run).  Shared
+  // real runs only, numbered sequence by sequence (locate_run).  Shared
   // prefix: item = (query tile, run, head group), head groups fastest; the
   // stream is table row 0 over the prefix, one partition per run.
   const int groups = Hkv / wpg;
