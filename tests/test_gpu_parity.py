@@ -525,3 +525,21 @@ def test_large_logits(pa, G, kv):
         out, lse = gpu_decode(pa, wl, d, partition_size=P)
         check_close(out.cpu().numpy(), want, f"large logits G={G} kv={kv} P={P}")
         np.testing.assert_allclose(lse.cpu().numpy(), want_lse, rtol=0, atol=1e-3)
+
+
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
+def test_run_longer_than_lds_id_buffer(pa, kv):
+    """A 32768-token partition is one run of 2048 blocks, more than the 1024
+    block ids the matrix-core kernel stages in LDS at a time, so the
+    workgroup refills its id buffer mid-run; a ragged second partition and
+    a tail block follow."""
+    over = dict(batch=1, q_heads=64, kv_heads=8, head_dim=128, ctx=40005, scatter=0.15,
+                kv_dtype=kv, partition_size=32768)
+    wl = gen.make("long128k_int8", seed=97 + len(kv), overrides=over)
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    d = device_inputs(wl, vals)
+    say(f"id buffer refill kv={kv} L={wl.max_context_len} P=32768")
+    out, lse = gpu_decode(pa, wl, d, partition_size=32768)
+    want, want_lse = oracle_decode(wl, vals)
+    check_close(out.cpu().numpy(), want, f"id refill kv={kv}")
+    np.testing.assert_allclose(lse.cpu().numpy(), want_lse, rtol=0, atol=1e-4)
