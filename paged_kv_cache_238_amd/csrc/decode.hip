@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
 
   // Start-up loads, all independent: length, first 64 block ids of the run
   // (clamped to the table row), Q.
-  const int L = p.context_lens[b] - p.token_offset;
+  const int L = rs.len >= 0 ? rs.len : p.context_lens[b] - p.token_offset;
   const int row_left = p.max_blocks - j0;
   const int span_blocks = span * (P / kBlockTokens);
   // Block ids c0 .. c0+63 of the run, one per lane, through a buffer

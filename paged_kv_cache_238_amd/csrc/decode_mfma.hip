@@ -224,7 +224,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   // prefix: item = (query tile, run, head group), head groups fastest; the
   // stream is table row 0 over the prefix, one partition per run.
   const int groups = Hkv / wpg;
-  int grp, b, ridx, span, tile = 0;
+  int grp, b, ridx, span, tile = 0, len = -1;
   if constexpr (PREFIX) {
     const int n_rg = p.n_part * groups;
     tile = blockIdx.x / n_rg;
@@ -240,6 +240,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     if (rs.b < 0) return;                    // past the last run
     b = rs.b;
     ridx = rs.ridx;
+    len = rs.len;
   }
   const int g = grp * wpg + w;
   const int h0 = g * G;
@@ -261,7 +262,8 @@ void decode_mfma_kernel(const DecodeParams p) {
       p.block_table + (size_t)b * p.bt_stride + p.token_offset / kBlockTokens;
 
   // Start-up loads, all independent: the length and Q.
-  const int L = PREFIX ? p.max_context_len : p.context_lens[b] - p.token_offset;
+  const int L = PREFIX ? p.max_context_len
+                       : len >= 0 ? len : p.context_lens[b] - p.token_offset;
   const int row_left = p.max_blocks - j0;
   const int span_blocks = span * (P / kBlockTokens);
   // The run's slice of the table row as a buffer resource: ids past the

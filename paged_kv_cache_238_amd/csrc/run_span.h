@@ -36,6 +36,7 @@ struct RunSlot {
   int b;      // sequence, or -1: no item for this workgroup
   int ridx;   // run index within the sequence
   int grp;    // head group (kv heads grp*wpg .. grp*wpg+wpg-1)
+  int len;    // context_lens[b] - token_offset when the search read it, else -1
 };
 
 // Cross-lane steps on the VALU (DPP and gfx950's permlane swaps) rather
@@ -83,7 +84,7 @@ __device__ inline int wave_scan(int x) {
 // context) the runs are the sequences themselves, empty or invalid ones
 // included: the kernel writes their rows.
 __device__ inline RunSlot locate_run(const DecodeParams& p, int groups) {
-  RunSlot r{1, -1, 0, (int)(blockIdx.x % groups)};
+  RunSlot r{1, -1, 0, (int)(blockIdx.x % groups), -1};
   const int item = blockIdx.x / groups;      // run number, head groups fastest
   if (p.direct) {
     if (item < p.batch) r.b = item;
@@ -101,13 +102,13 @@ __device__ inline RunSlot locate_run(const DecodeParams& p, int groups) {
   const int lane = threadIdx.x & 63;
   const int P = p.partition_size;
   const int max_part = (p.max_context_len + P - 1) / P;
-  auto parts = [&](int b) {                  // partitions of sequence b (0 if invalid)
-    if (b >= p.batch) return 0;
-    const int L = p.context_lens[b] - p.token_offset;
+  auto length = [&](int b) { return b < p.batch ? p.context_lens[b] - p.token_offset : 0; };
+  auto parts_in = [&](int L) {               // partitions of a length (0 if invalid)
     return (L > 0 && L <= p.max_context_len) ? (L + P - 1) / P : 0;
   };
-  const int n0 = parts(lane);                // batches of up to 64 need one load
-  auto parts_of = [&](int b0) { return b0 == 0 ? n0 : parts(b0 + lane); };
+  const int len0 = length(lane);             // batches of up to 64 need one load
+  const int n0 = parts_in(len0);
+  auto parts_of = [&](int b0) { return b0 == 0 ? n0 : parts_in(length(b0 + lane)); };
   // span: the smallest run length (in partitions) that leaves at most
   // target_waves (run, kv head) items; items(s) does not grow with s, and at
   // s = max_part every sequence is one run (batch * kv_heads < target).
@@ -139,6 +140,8 @@ __device__ inline RunSlot locate_run(const DecodeParams& p, int groups) {
       // lane owns it
       const int k = (int)__builtin_popcountll(__ballot(base + incl <= item));
       r.b = b0 + k;
+      // the owner's length, already loaded: the kernel need not read it again
+      r.len = __builtin_amdgcn_readlane(b0 == 0 ? len0 : length(b0 + lane), k);
       r.ridx = item - base - (__builtin_amdgcn_readlane(incl, k) -
                               __builtin_amdgcn_readlane(runs, k));
       return r;
