@@ -130,15 +130,22 @@ def test_shared_prefix_validation(kw, code):
 
 
 def test_shared_prefix_workspace_size():
-    # header; suffix records over ceil((1536 - 1024) / 256) = 2 partitions;
+    # header; suffix records: a 512-token suffix is 32 blocks, at most eight
+    # partitions of 4 blocks (64 tokens), so 8 of them;
     # prefix records: 4 query tiles x 32 kv heads = 128 waves per prefix
     # partition, so 128-token partitions (about 1024 waves), 8 of them;
     # 256-byte aligned parts
     rows = 64 * 32
-    suf = 256 + rows * 2 * 8 + rows * 2 * 512
+    suf = 256 + rows * 8 * 8 + rows * 8 * 512
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
         suf + rows * 8 * 8 + rows * 8 * 512
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1000) == 0
+    # longer suffixes: 4096 - 1024 = 3072 tokens, 192 blocks; partitions of
+    # 24 blocks would exceed 256 tokens, so 256 (12 partitions); prefix: one
+    # query tile x 8 kv heads = 8 waves per partition, so one-block
+    # partitions, 64 of them
+    assert pa.shared_prefix_workspace_size(8, 8, 8, 128, 4096, 1024) == \
+        256 + 64 * 12 * (8 + 512) + 64 * 64 * (8 + 512)
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1024, 1024) == \
         256 + rows * (8 + 512) + rows * 8 * (8 + 512)
     # few queries: 2 tiles x 8 kv heads = 16 waves per partition, so the
