@@ -160,8 +160,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   const int32_t* bt_row =
       p.block_table + (size_t)b * p.bt_stride + p.token_offset / kBlockTokens;
 
-  // Start-up loads, all independent: length, first 64 block ids of the run
-  // (clamped to the table row), Q.
+  // Start-up loads, independent of each other: the length (unless the run
+  // search already read it), the first 64 block ids of the run (clamped to
+  // the table row) and Q.
   const int L = rs.len >= 0 ? rs.len : p.context_lens[b] - p.token_offset;
   const int row_left = p.max_blocks - j0;
   const int span_blocks = span * (P / kBlockTokens);

@@ -261,7 +261,8 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int32_t* bt_row =
       p.block_table + (size_t)b * p.bt_stride + p.token_offset / kBlockTokens;
 
-  // Start-up loads, all independent: the length and Q.
+  // Start-up loads, independent of each other: the length (unless the run
+  // search already read it) and Q.
   const int L = PREFIX ? p.max_context_len
                        : len >= 0 ? len : p.context_lens[b] - p.token_offset;
   const int row_left = p.max_blocks - j0;
