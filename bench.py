@@ -76,7 +76,7 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("decode.hip", "decode_mfma.hip", "merge.hip", "run_span.h", "pa_internal.h",
+KERNEL_SOURCES = ("decode.hip", "decode_mfma.hip", "merge.hip", "work_split.h", "pa_internal.h",
                   "pa_api.hip", "write_kv.hip")
 
 

@@ -166,9 +166,9 @@ int pa_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
 /*
  * Partition size the library uses for these shapes when partition_size is
  * 0, else partition_size itself (a multiple of 16).  The library's choice:
- * 256 tokens, the finest split, with runs of partitions merged on the
- * device (see the workspace layout below); or, when batch * kv_heads alone
- * reaches 2048 (enough waves to fill the GPU), one partition covering
+ * 256 tokens, the finest split, with the work cut into balanced chunks on
+ * the device (see the workspace layout below); or, when batch * kv_heads
+ * alone reaches 2048 (enough waves to fill the GPU), one partition covering
  * max_context_len rounded up to 16, so no merge runs.  Returns 0 on invalid
  * arguments.
  */
@@ -246,31 +246,42 @@ int pa_decode_fp8(void* out, float* lse_out, const void* q, const uint8_t* k_poo
  * partition records into the workspace, which must hold
  * pa_decode_workspace_size(..., partition_size resolved, ...) bytes
  * computed with max_context_len > partition_size, i.e. room for
- * n_part = ceil(max_context_len / P) records per (b, h).  Workspace layout
- * (P = resolved partition size):
- *   int32  header[64]                   header[0] = span: partitions per
- *                                       record.  Record r of (b, h) covers
- *                                       partitions [r*span, (r+1)*span).
- *                                       span is chosen on the device from
- *                                       the context lengths: the smallest
- *                                       span that leaves at most 2048
- *                                       (record, kv head) runs over the
- *                                       batch (1 when batch * kv_heads
- *                                       alone reaches 2048); one wave
- *                                       merges a run's partitions online.
- *   float2 ml[batch][q_heads][n_part]   (m, l): m = a reference point in
- *                                       log2 units, at most the partition's
+ * n_part + 1 records per (b, h), n_part = ceil(max_context_len / P).
+ * Workspace layout (P = resolved partition size):
+ *   int32  header[64 + batch]           header[0] = record mode:
+ *                                       1 when batch * kv_heads >= 2048:
+ *                                         record r covers partition r,
+ *                                         tokens [rP, min((r+1)P, L_b));
+ *                                       0 otherwise (balanced chunks): the
+ *                                         blocks of all sequences, laid end
+ *                                         to end in batch order (sequence b
+ *                                         owns blocks [F_b, F_b + nb_b),
+ *                                         nb_b = ceil(L_b / 16), 0 for an
+ *                                         empty or invalid length), are cut
+ *                                         into chunks of C = max(P / 16,
+ *                                         ceil(T / floor(2048 / kv_heads)))
+ *                                         blocks, T = sum nb_b; record r of
+ *                                         b covers b's blocks in chunk
+ *                                         floor(F_b / C) + r, and
+ *                                         header[64 + b] holds b's record
+ *                                         count (written for L_b > 0 only).
+ *                                       One wave streams a chunk's blocks
+ *                                       for one kv head and merges them
+ *                                       online, one record per sequence.
+ *                                       The header takes 256-byte units.
+ *   float2 ml[batch][q_heads][n_part+1] (m, l): m = a reference point in
+ *                                       log2 units, at most the record's
  *                                       largest score s = scale * log2(e) *
  *                                       q.k (and within 8 of it); l = sum of
  *                                       2^(s - m); m + log2(l) is the
- *                                       partition's log-sum-exp
- *   float  o[batch][q_heads][n_part][head_dim]  unnormalised sum 2^(s-m) v
+ *                                       record's log-sum-exp
+ *                                       (256-byte aligned after the header)
+ *   float  o[batch][q_heads][n_part+1][head_dim]  unnormalised sum 2^(s-m) v
  *                                       (256-byte aligned after ml)
- * Records at or past ceil(ceil(L_b / P) / span) are not written.
+ * Records past a row's count are not written.
  *
  * pa_merge_partials: out[b,h] = sum_r 2^(m_r - M) o_r / sum_r 2^(m_r - M) l_r
- * over the records r < ceil(ceil(L_b / P) / span), M = max m_r;
- * lse = ln 2 * (M + log2(den)).
+ * over the row's records, M = max m_r; lse = ln 2 * (M + log2(den)).
  */
 int pa_decode_partials(const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, int max_blocks,

@@ -3,11 +3,13 @@
 // kernel in decode_mfma.hip).
 //
 // Work split (as in the matrix-core kernel): a workgroup holds up to four
-// waves for consecutive kv heads of one (sequence, run); each wave streams
-// its head's run of partitions - sized on the device from the actual
-// context lengths (run_span.h) - merges it online and writes one record
-// (max reference, sum, unnormalised output) for the log-sum-exp merge
-// kernel, or the final fp16 row when one partition covers the context.
+// waves for consecutive kv heads of one work item - a balanced chunk of
+// blocks sized on the device from the actual context lengths
+// (work_split.h), a partition, or a whole sequence; each wave streams its
+// head's blocks of the item, merges them online and writes one record (max
+// reference, sum, unnormalised output) per sequence the item reaches, for
+// the log-sum-exp merge kernel, or the final fp16 row when one partition
+// covers the context.
 //
 // Method: the zskr.cn article on ATB's PagedAttention, section
 // "PagedAttention 的 Attention 计算修改" - per-page gather through the page
@@ -25,10 +27,10 @@
 // int8), so one wave-wide load covers 64/(D/8) token rows.  Lanes holding
 // the same token ("row group") reduce their partial dot products with DPP;
 // every row group keeps its own running (max, sum, acc) so the hot loop has
-// no cross-row traffic; row groups are merged once per run.  Scores are
+// no cross-row traffic; row groups are merged once per segment.  Scores are
 // kept in log2 units (scale * log2 e folded in), so exp is one v_exp_f32.
 #include "pa_internal.h"
-#include "run_span.h"
+#include "work_split.h"
 
 #include <type_traits>
 
@@ -143,34 +145,56 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   const int r = lane / LPR, c = lane % LPR;
   const int Hq = p.q_heads, Hkv = p.kv_heads;
 
-  // Workgroup item = (run, head group), assigned on the device over the
-  // real runs only, numbered sequence by sequence (locate_run).
+  // Workgroup item: a balanced chunk of blocks, a (partition, sequence) or a
+  // sequence, with a head group (locate_work).  A chunk may cross sequence
+  // boundaries; each sequence it reaches is one segment with its own record.
   const int groups = Hkv / wpg;
-  const RunSlot rs = locate_run(p, groups);
-  const int span = rs.span;
-  const int g = rs.grp * wpg + w;
+  Segment sg = locate_work(p, groups);
+  const int g = sg.grp * wpg + w;
   const int h0 = g * G;
-  if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = span;
-  if (rs.b < 0) return;                      // past the last run
-  const int b = rs.b, ridx = rs.ridx;
+  if (!p.direct && blockIdx.x == 0 && tid == 0)
+    p.header[0] = (long long)p.batch * Hkv >= p.target_waves ? 1 : 0;
+  if (sg.b < 0) return;                      // no work for this workgroup
 
-  const int P = p.partition_size;
-  const int t_begin = ridx * span * P;
-  const int j0 = min(t_begin / kBlockTokens, p.max_blocks - 1);
+  // Addressing: a block's rows for kv head g start at a wave-uniform base
+  // (scalar registers); each lane adds a fixed 32-bit offset per load.
+  const uint32_t blk_bytes = (uint32_t)kBlockTokens * Hkv * D * ESZ;
+  uint32_t lane_off[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    lane_off[i] = ((uint32_t)(r + RPW * i) * Hkv * D + (uint32_t)g * D + (uint32_t)c * 8) * ESZ;
+  uint32_t scale_off[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) scale_off[i] = (uint32_t)g * kBlockTokens + r + RPW * i;   // [NB, Hkv, 16]
+  const char* kbase = static_cast<const char*>(p.k_pool);
+  const char* vbase = static_cast<const char*>(p.v_pool);
+  const uint32_t scale_blk_bytes = (uint32_t)kBlockTokens * Hkv * sizeof(float);
+
+  do {                                       // segments of the item
+  note_record_count(p, sg, w == 0 && lane == 0);
+  // The segment's fields are wave-uniform; saying so keeps every value
+  // derived from them (lengths, block counts, buffer resources) in scalar
+  // registers across the segment loop.
+  const int b = __builtin_amdgcn_readfirstlane(sg.b);
+  const int ridx = __builtin_amdgcn_readfirstlane(sg.rec);
+  const int seg_j0 = __builtin_amdgcn_readfirstlane(sg.j0);
+  const int seg_blocks = __builtin_amdgcn_readfirstlane(sg.nblk);
+  const int seg_len = __builtin_amdgcn_readfirstlane(sg.len);
+  const int t_begin = seg_j0 * kBlockTokens;
+  const int j0 = min(seg_j0, p.max_blocks - 1);
   const int32_t* bt_row =
       p.block_table + (size_t)b * p.bt_stride + p.token_offset / kBlockTokens;
 
-  // Start-up loads, independent of each other: the length (unless the run
-  // search already read it), the first 64 block ids of the run (clamped to
-  // the table row) and Q.
-  const int L = rs.len >= 0 ? rs.len : p.context_lens[b] - p.token_offset;
+  // Start-up loads, independent of each other: the length (unless the
+  // search already read it), the first 64 block ids of the segment (clamped
+  // to the table row) and Q.
+  const int L = seg_len >= 0 ? seg_len : p.context_lens[b] - p.token_offset;
   const int row_left = p.max_blocks - j0;
-  const int span_blocks = span * (P / kBlockTokens);
-  // Block ids c0 .. c0+63 of the run, one per lane, through a buffer
-  // resource bounded to the run's slice of the table row: ids past the
+  // Block ids c0 .. c0+63 of the segment, one per lane, through a buffer
+  // resource bounded to the segment's slice of the table row: ids past the
   // slice read as 0 with no branch, so the load stays asynchronous.
   const __amdgpu_buffer_rsrc_t rids =
-      make_rsrc(bt_row + j0, (uint32_t)max(min(span_blocks, row_left), 0) * 4u);
+      make_rsrc(bt_row + j0, (uint32_t)max(min(seg_blocks, row_left), 0) * 4u);
   auto load_ids = [&](int c0) {
     return (int)__builtin_amdgcn_raw_buffer_load_b32(rids, (uint32_t)(c0 + lane) * 4u, 0, 0);
   };
@@ -181,6 +205,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   for (int hh = 0; hh < G; ++hh)
     qraw[hh] = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * Hq + h0 + hh) * D + c * 8);
 
+  // Empty or broken sequences only reach here as single-segment items
+  // (direct mode or partition items); chunks skip them.
   if (L < 0 || L > p.max_context_len) {      // broken metadata: NaN rows
     if (ridx == 0 && p.direct) {
       for (int i = lane; i < G * D; i += 64) {
@@ -191,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     }
     return;
   }
-  if (t_begin >= L) {                        // empty run (L == 0: zero row)
+  if (t_begin >= L) {                        // empty item (L == 0: zero row)
     if (p.direct && ridx == 0) {
       for (int i = lane; i < G * D; i += 64) {
         const size_t row = (size_t)b * Hq + h0 + i / D;
@@ -201,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     }
     return;
   }
-  const int ntok = min(t_begin + span_blocks * kBlockTokens, L) - t_begin;
+  const int ntok = min(t_begin + seg_blocks * kBlockTokens, L) - t_begin;
   const int nfull = ntok / kBlockTokens;
   const int tail = ntok - nfull * kBlockTokens;
 
@@ -220,20 +246,6 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
   }
   bool bad_blk = false;
-
-  // Addressing: a block's rows for kv head g start at a wave-uniform base
-  // (scalar registers); each lane adds a fixed 32-bit offset per load.
-  const uint32_t blk_bytes = (uint32_t)kBlockTokens * Hkv * D * ESZ;
-  uint32_t lane_off[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i)
-    lane_off[i] = ((uint32_t)(r + RPW * i) * Hkv * D + (uint32_t)g * D + (uint32_t)c * 8) * ESZ;
-  uint32_t scale_off[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) scale_off[i] = (uint32_t)g * kBlockTokens + r + RPW * i;   // [NB, Hkv, 16]
-  const char* kbase = static_cast<const char*>(p.k_pool);
-  const char* vbase = static_cast<const char*>(p.v_pool);
-  const uint32_t scale_blk_bytes = (uint32_t)kBlockTokens * Hkv * sizeof(float);
 
   struct Regs {
     Chunk k[NL];
@@ -346,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     }
   };
 
-  // Record of the run: merge the RPW row groups, then store.
+  // Record of the segment: merge the RPW row groups, then store.
   auto finalize = [&]() {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -380,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
           *reinterpret_cast<uint4*>(p.out + row * D + c * 8) = pk;
           if (c == 0 && p.lse) p.lse[row] = (M + log2f(den)) * kLn2;
         } else {
-          const size_t rec = row * p.n_part + ridx;
+          const size_t rec = row * p.rec_stride + ridx;
           float4* dst = reinterpret_cast<float4*>(p.part_o + rec * D + c * 8);
           float4 a = make_float4(o[0], o[1], o[2], o[3]);
           float4 bq = make_float4(o[4], o[5], o[6], o[7]);
@@ -393,13 +405,13 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     }
   };
 
-  // Blocks of the run, streamed in order.  Block ids come one per lane from
+  // Blocks of the segment, streamed in order.  Block ids come one per lane from
   // `ids`, a 64-block chunk; the following chunk is fetched into `ids_next`
   // a whole chunk ahead and moved over just before its first block is
   // issued, so no issue reads a register whose load may still be pending.
   // Two register sets alternate, so one block is in flight while the other
   // is reduced; block j always lands in R[j % 2].  The partial last block
-  // (only in a sequence's last run) is fetched through the same pipeline as
+  // (only in a sequence's last segment) is fetched through the same pipeline as
   // block nfull and reduced after the loop; later prefetches read nothing
   // (empty resource) and, with two sets, never land on the tail's set.
   // Every branch is wave-uniform and no load sits inside one, so the waits
@@ -441,6 +453,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
       process_block(last, R[0], tail);
   }
   finalize();
+  } while (next_segment(p, sg));
 }
 
 // Waves (kv heads) per workgroup: four when the heads divide evenly.

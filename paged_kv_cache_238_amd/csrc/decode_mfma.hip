@@ -29,7 +29,7 @@
 // staged on chip once per workgroup, section "踩坑一"; query heads grouped on
 // one K/V head, discosf.com article, section "二、优化方向").
 #include "pa_internal.h"
-#include "run_span.h"
+#include "work_split.h"
 
 #include <type_traits>
 
@@ -44,7 +44,7 @@ typedef short s4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;   // at most eight waves (kv heads) per workgroup
-// Block ids of a run staged in LDS per workgroup, refilled kIdCap at a time.
+// Block ids of a segment staged in LDS per workgroup, refilled kIdCap at a time.
 constexpr int kIdCap = 1024;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.693147180559945309f;
@@ -196,10 +196,11 @@ __device__ __forceinline__ float scale_of(float x, int i) {
 // four waves per SIMD with fewer sets both measured slower.
 //
 // Work split: a workgroup holds `wpg` waves (1, 2, 4 or 8) for wpg consecutive
-// kv heads of one (sequence, partition); each wave streams its own head's
-// whole partition and writes its own record.  The waves of a workgroup thus
-// read neighbouring slices of the same token rows at the same time, and a
-// wave's start-up (length, block ids, Q) is paid once per partition.
+// kv heads of one work item (work_split.h); each wave streams its own head's
+// blocks of the item and writes its own record per sequence.  The waves of a
+// workgroup thus read neighbouring slices of the same token rows at the same
+// time, and a wave's start-up (lengths, block ids, Q) is paid once per
+// segment.
 template <int D, int G, int KV, bool PREFIX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES_PER_EU)))
 void decode_mfma_kernel(const DecodeParams p) {
@@ -219,31 +220,65 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int li = lane & 15;       // index in group: token row for loads, head for softmax
   const int Hq = p.q_heads, Hkv = p.kv_heads;
 
-  // Workgroup item = (run, head group), assigned on the device over the
-  // real runs only, numbered sequence by sequence (locate_run).  Shared
-  // prefix: item = (query tile, run, head group), head groups fastest; the
-  // stream is table row 0 over the prefix, one partition per run.
+  // Workgroup item: a balanced chunk of blocks, a (partition, sequence) or a
+  // sequence, with a head group (locate_work); a chunk may cross sequence
+  // boundaries, and each sequence it reaches is one segment with its own
+  // record.  Shared prefix: item = (query tile, partition, head group), head
+  // groups fastest; the stream is table row 0 over the prefix.
   const int groups = Hkv / wpg;
-  int grp, b, ridx, span, tile = 0, len = -1;
+  Segment sg;
+  int tile = 0;
   if constexpr (PREFIX) {
     const int n_rg = p.n_part * groups;
     tile = blockIdx.x / n_rg;
-    ridx = (blockIdx.x % n_rg) / groups;
-    grp = blockIdx.x % groups;
-    b = 0;
-    span = 1;
+    const int part = (blockIdx.x % n_rg) / groups;
+    sg = Segment{0, -1, part * (p.partition_size / kBlockTokens),
+                 p.partition_size / kBlockTokens, part, (int)(blockIdx.x % groups), 0, 0, -1, 0};
   } else {
-    const RunSlot rs = locate_run(p, groups);
-    span = rs.span;
-    grp = rs.grp;
-    if (!p.direct && blockIdx.x == 0 && tid == 0) p.header[0] = span;
-    if (rs.b < 0) return;                    // past the last run
-    b = rs.b;
-    ridx = rs.ridx;
-    len = rs.len;
+    sg = locate_work(p, groups);
+    if (!p.direct && blockIdx.x == 0 && tid == 0)
+      p.header[0] = (long long)p.batch * Hkv >= p.target_waves ? 1 : 0;
+    if (sg.b < 0) return;                    // no work for this workgroup
   }
-  const int g = grp * wpg + w;
+  const int g = sg.grp * wpg + w;
   const int h0 = g * G;
+
+  char* s_tile = smem + w * TILE;            // this wave's V tile
+  // Block ids of the segment, shared by the workgroup (all its waves stream
+  // the same blocks, so every step below is taken by all of them together).
+  int32_t* s_ids = reinterpret_cast<int32_t*>(smem + wpg * TILE);
+
+  const uint32_t row_bytes = (uint32_t)Hkv * D * ESZ;          // one token row, all heads
+  const uint32_t blk_bytes = (uint32_t)kBlockTokens * row_bytes;
+  // Offsets of this lane's loads within a block, and their V tile targets.
+  uint32_t ld_off[NLD];
+  uint32_t ld_lds[NLD];
+  int ld_row[NLD];
+#pragma unroll
+  for (int ld = 0; ld < NLD; ++ld) {
+    ld_row[ld] = Geo::load_row(ld, lane);
+    const int col = Geo::load_col(ld, lane);
+    ld_off[ld] = (uint32_t)ld_row[ld] * row_bytes + (uint32_t)g * D * ESZ + (uint32_t)col;
+    ld_lds[ld] = (uint32_t)ld_row[ld] * Geo::kRowBytes + (uint32_t)(col / ESZ) * 2;
+  }
+  const char* kbase = static_cast<const char*>(p.k_pool);
+  const char* vbase = static_cast<const char*>(p.v_pool);
+  const uint32_t scale_blk_bytes = (uint32_t)kBlockTokens * Hkv * sizeof(float);
+
+  // LDS addresses of this lane's transposed V reads: tile nb, group lg reads
+  // token rows 4*lg + li/4 at dims 16*nb + 4*(li%4) (8 bytes each).
+  const uint32_t tr_base = (uint32_t)(4 * lg + li / 4) * Geo::kRowBytes + (uint32_t)(4 * (li % 4)) * 2;
+
+  do {                                       // segments of the item
+  if constexpr (!PREFIX) note_record_count(p, sg, tid == 0);
+  // The segment's fields are wave-uniform; saying so keeps every value
+  // derived from them (lengths, block counts, buffer resources) in scalar
+  // registers across the segment loop.
+  const int b = __builtin_amdgcn_readfirstlane(sg.b);
+  const int ridx = __builtin_amdgcn_readfirstlane(sg.rec);
+  const int seg_j0 = __builtin_amdgcn_readfirstlane(sg.j0);
+  const int seg_blocks = __builtin_amdgcn_readfirstlane(sg.nblk);
+  const int seg_len = __builtin_amdgcn_readfirstlane(sg.len);
   // Row of q / out / records of query slot li, or -1 for a padding slot.
   int qrow = -1;
   if constexpr (PREFIX) {
@@ -254,23 +289,20 @@ void decode_mfma_kernel(const DecodeParams p) {
     if (li < G) qrow = b * Hq + h0 + li;
   }
 
-  const int P = p.partition_size;
-  const int part0 = ridx * span;             // first partition of this run
-  const int t_begin = part0 * P;
-  const int j0 = min(t_begin / kBlockTokens, p.max_blocks - 1);
+  const int t_begin = seg_j0 * kBlockTokens;
+  const int j0 = min(seg_j0, p.max_blocks - 1);
   const int32_t* bt_row =
       p.block_table + (size_t)b * p.bt_stride + p.token_offset / kBlockTokens;
 
-  // Start-up loads, independent of each other: the length (unless the run
+  // Start-up loads, independent of each other: the length (unless the
   // search already read it) and Q.
   const int L = PREFIX ? p.max_context_len
-                       : len >= 0 ? len : p.context_lens[b] - p.token_offset;
+                       : seg_len >= 0 ? seg_len : p.context_lens[b] - p.token_offset;
   const int row_left = p.max_blocks - j0;
-  const int span_blocks = span * (P / kBlockTokens);
-  // The run's slice of the table row as a buffer resource: ids past the
+  // The segment's slice of the table row as a buffer resource: ids past the
   // slice read as 0 with no branch.
   const __amdgpu_buffer_rsrc_t rids =
-      make_rsrc(bt_row + j0, (uint32_t)max(min(span_blocks, row_left), 0) * 4u);
+      make_rsrc(bt_row + j0, (uint32_t)max(min(seg_blocks, row_left), 0) * 4u);
 
   // Q^T as the B operand of the QK product: lane holds Q[slot li][dim(kk, lg, j)].
   // Each step's 8 dims are consecutive (Geo::dim), so one 16-byte load each;
@@ -286,6 +318,8 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
   }
 
+  // Empty or broken sequences only reach here as single-segment items
+  // (direct mode or partition items); chunks skip them.
   if (L < 0 || L > p.max_context_len) {      // broken metadata: NaN rows
     if (ridx == 0 && p.direct && qrow >= 0) {
       const size_t row = (size_t)qrow;
@@ -294,7 +328,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
     return;
   }
-  if (t_begin >= L) {                        // empty run (L == 0: zero row)
+  if (t_begin >= L) {                        // empty item (L == 0: zero row)
     if (p.direct && ridx == 0 && qrow >= 0) {
       const size_t row = (size_t)qrow;
       for (int d = lg; d < D; d += 4) p.out[row * D + d] = 0;
@@ -302,16 +336,12 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
     return;
   }
-  const int ntok = min(t_begin + span_blocks * kBlockTokens, L) - t_begin;
+  const int ntok = min(t_begin + seg_blocks * kBlockTokens, L) - t_begin;
   const int nfull = ntok / kBlockTokens;
   const int tail = ntok - nfull * kBlockTokens;
 
-  char* s_tile = smem + w * TILE;            // this wave's V tile
-  // Block ids of the run, shared by the workgroup (all its waves stream the
-  // same run, so every step below is taken by all of them together).  Ids
-  // come from LDS in order, each read NBUF blocks before its block is
+  // Ids come from LDS in order, each read NBUF blocks before its block is
   // issued, so no block waits on a table read.
-  int32_t* s_ids = reinterpret_cast<int32_t*>(smem + wpg * TILE);
   auto fill_ids = [&](int base) {            // ids base .. base + kIdCap - 1
     __syncthreads();                         // the previous chunk is read
     for (int t = tid; t < kIdCap; t += blockDim.x)
@@ -337,27 +367,6 @@ void decode_mfma_kernel(const DecodeParams p) {
   float m_run = kNegInf;   // reference max of head li (same in all four lane groups)
   float l_run = 0.f;       // this lane's share of the running sum (its tokens)
   bool bad_blk = false;
-
-  const uint32_t row_bytes = (uint32_t)Hkv * D * ESZ;          // one token row, all heads
-  const uint32_t blk_bytes = (uint32_t)kBlockTokens * row_bytes;
-  // Offsets of this lane's loads within a block, and their V tile targets.
-  uint32_t ld_off[NLD];
-  uint32_t ld_lds[NLD];
-  int ld_row[NLD];
-#pragma unroll
-  for (int ld = 0; ld < NLD; ++ld) {
-    ld_row[ld] = Geo::load_row(ld, lane);
-    const int col = Geo::load_col(ld, lane);
-    ld_off[ld] = (uint32_t)ld_row[ld] * row_bytes + (uint32_t)g * D * ESZ + (uint32_t)col;
-    ld_lds[ld] = (uint32_t)ld_row[ld] * Geo::kRowBytes + (uint32_t)(col / ESZ) * 2;
-  }
-  const char* kbase = static_cast<const char*>(p.k_pool);
-  const char* vbase = static_cast<const char*>(p.v_pool);
-  const uint32_t scale_blk_bytes = (uint32_t)kBlockTokens * Hkv * sizeof(float);
-
-  // LDS addresses of this lane's transposed V reads: tile nb, group lg reads
-  // token rows 4*lg + li/4 at dims 16*nb + 4*(li%4) (8 bytes each).
-  const uint32_t tr_base = (uint32_t)(4 * lg + li / 4) * Geo::kRowBytes + (uint32_t)(4 * (li % 4)) * 2;
 
   struct Regs {
     uint4 k[NLD];
@@ -492,7 +501,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
   };
 
-  // Record of the run (relative to m_run).
+  // Record of the segment (relative to m_run).
   // Lane (lg, li) holds O[head li][dim 16n + 4lg + i].
   auto finalize = [&]() {
     float den = l_run;
@@ -515,7 +524,7 @@ void decode_mfma_kernel(const DecodeParams p) {
         }
         if (lg == 0 && p.lse) p.lse[row] = (M + log2f(den)) * kLn2;
       } else {
-        const size_t rec = row * p.n_part + ridx;
+        const size_t rec = row * p.rec_stride + ridx;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           f4 o = acc[n];
@@ -527,7 +536,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
   };
 
-  // Full blocks of the run, streamed in order.  Register sets rotate so that
+  // Full blocks of the segment, streamed in order.  Register sets rotate so that
   // NBUF - 1 blocks are in flight while one is reduced (int8 blocks are half
   // the bytes, so they go one deeper); prefetches past the end read nothing.
   // Block ids: each register set carries nid, the id of the next block it
@@ -547,7 +556,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     auto issue = [&](int j, int slot, int blk) {
       load_block(blk, j < nfull, R[slot]);
       if (j + NBUF - id_base >= kIdCap && j + NBUF < nfull) {
-        fill_ids(j + NBUF);                  // rare: runs longer than kIdCap blocks
+        fill_ids(j + NBUF);                  // rare: segments longer than kIdCap blocks
         id_base = j + NBUF;
       }
       nid[slot] = lds_id(j + NBUF);
@@ -571,19 +580,20 @@ void decode_mfma_kernel(const DecodeParams p) {
       }
     }
   }
-  // The partial last block (only in a sequence's last run).
+  // The partial last block (only in a sequence's last segment).
   if (tail > 0) {
     Regs T;
     load_block(__builtin_amdgcn_readfirstlane(tail_id), true, T);
     process_block(std::integral_constant<bool, true>(), T, tail);
   }
   finalize();
+  } while (!PREFIX && next_segment(p, sg));
 }
 
-// Waves (kv heads) per workgroup.  Long contexts (runs of many blocks, all
+// Waves (kv heads) per workgroup.  Long contexts (chunks of many blocks, all
 // alike): eight, so one workgroup reads whole token rows of an 8-head cache.
 // Otherwise four, which keeps workgroups small enough to pack CUs evenly
-// when runs are short or uneven.
+// when chunks are short or uneven.
 int waves_per_group(const DecodeParams& p) {
   if (p.kv_heads % 8 == 0 && p.max_context_len >= kLongContext) return 8;
   return (p.kv_heads % 4 == 0) ? 4 : (p.kv_heads % 2 == 0) ? 2 : 1;

@@ -1,16 +1,17 @@
 // Log-sum-exp merge of split-K partition records into the final fp16 row.
 //
-// Record r of sequence b, query head h carries (m_r, l_r, o_r) for a run of
-// `span` consecutive partitions (span from the workspace header): a
-// reference point m_r for its scores (log2 units), the sum of 2^(s - m_r)
-// and the unnormalised sum of 2^(s - m_r) v.  With M = max_p m_p and w_p = 2^(m_p - M):
+// Record r of sequence b, query head h carries (m_r, l_r, o_r) for one
+// stretch of its blocks (a partition, or a balanced chunk's share of the
+// sequence, as the workspace header says): a reference point m_r for its
+// scores (log2 units), the sum of 2^(s - m_r) and the unnormalised sum of
+// 2^(s - m_r) v.  With M = max_p m_p and w_p = 2^(m_p - M):
 //   out = sum_p w_p o_p / sum_p w_p l_p,   lse = ln2 * (M + log2 sum_p w_p l_p).
 // This is the running-max rescaling of the zskr.cn article's PagedAttention
 // kernel (section "PagedAttention 的 Attention 计算修改") applied once
 // across partitions instead of token by token, followed by that kernel's
 // final normalisation and fp16 store.
 //
-// Rows with at most 32 records (the partition count bounds them): one wave
+// Rows with at most 17 * 256 / D records (the record stride bounds them): one wave
 // per (sequence, query head), four rows per workgroup; lanes are D/4 float4
 // columns x 256/D record phases, every record a lane needs is loaded at
 // once (one memory round trip), and the phases are added by shuffles in a
@@ -18,7 +19,7 @@
 // columns x 1024/D phases, phases added through LDS in a fixed order.  Both
 // are deterministic.
 //
-// Shared-prefix decode merges two record sets per row: the runs over the
+// Shared-prefix decode merges two record sets per row: the records over the
 // private suffix [prefix, L) and n_pre records over the shared prefix;
 // both enter the same sums (the log-sum-exp merge is associative).
 #include "pa_internal.h"
@@ -41,6 +42,14 @@ __device__ __forceinline__ float block_max(float x, float* s_max) {
 #pragma unroll
   for (int i = 1; i < kThreads / 64; ++i) x = fmaxf(x, s_max[i]);
   return x;
+}
+
+// Records the partition kernel wrote for a sequence of (valid) length L:
+// one per partition, or the count its balanced chunks stored in the header.
+__device__ __forceinline__ int suffix_records(const MergeParams& p, int b, int L) {
+  if (L == 0) return 0;
+  if (p.header[0] == 0) return p.header[kCountsAt + b];
+  return (L + p.partition_size - 1) / p.partition_size;
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
@@ -66,19 +75,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
     if (tid == 0 && p.lse) p.lse[row] = __builtin_nanf("");
     return;
   }
-  // records cover runs of `span` partitions (written by the partition kernel)
-  const int span = max(1, p.header[0]);
-  const int n_part_b = (L + p.partition_size - 1) / p.partition_size;
-  const int n_suf = (n_part_b + span - 1) / span;
+  const int n_suf = suffix_records(p, b, L);
   const int n_pre = p.pre_ml ? p.n_pre : 0;
-  const int n = n_suf + n_pre;               // records: suffix runs, then prefix
+  const int n = n_suf + n_pre;               // records: suffix, then prefix
   if (n == 0) {
     for (int d = tid; d < D; d += kThreads) p.out[row * D + d] = 0;
     if (tid == 0 && p.lse) p.lse[row] = kNegInf;
     return;
   }
-  const float2* ml = p.part_ml + row * p.n_part;
-  const float4* o = reinterpret_cast<const float4*>(p.part_o + row * p.n_part * D);
+  const float2* ml = p.part_ml + row * p.rec_stride;
+  const float4* o = reinterpret_cast<const float4*>(p.part_o + row * p.rec_stride * D);
   const float2* ml2 = n_pre ? p.pre_ml + row * n_pre : nullptr;
   const float4* o2 = n_pre ? reinterpret_cast<const float4*>(p.pre_o + row * n_pre * D) : nullptr;
   auto rec_ml = [&](int i) { return i < n_suf ? ml[i] : ml2[i - n_suf]; };
@@ -158,7 +164,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
   }
 }
 
-constexpr int kWaveHeld = 16;   // records per lane in the wave-per-row kernel
+constexpr int kWaveHeld = 17;   // records per lane in the wave-per-row kernel (34 at D = 128:
+                                // n_part + 1 records for 32 partitions)
 constexpr int kRowsPerGroup = kThreads / 64;
 
 template <int D>
@@ -176,9 +183,7 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(const MergeParams 
     if (lane == 0 && p.lse) p.lse[row] = __builtin_nanf("");
     return;
   }
-  const int span = max(1, p.header[0]);
-  const int n_part_b = (L + p.partition_size - 1) / p.partition_size;
-  const int n_suf = (n_part_b + span - 1) / span;
+  const int n_suf = suffix_records(p, b, L);
   const int n_pre = p.pre_ml ? p.n_pre : 0;
   const int n = n_suf + n_pre;
   if (n == 0) {
@@ -186,8 +191,8 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(const MergeParams 
     if (lane == 0 && p.lse) p.lse[row] = kNegInf;
     return;
   }
-  const float2* ml = p.part_ml + row * p.n_part;
-  const float4* o = reinterpret_cast<const float4*>(p.part_o + row * p.n_part * D);
+  const float2* ml = p.part_ml + row * p.rec_stride;
+  const float4* o = reinterpret_cast<const float4*>(p.part_o + row * p.rec_stride * D);
   const float2* ml2 = n_pre ? p.pre_ml + row * n_pre : nullptr;
   const float4* o2 = n_pre ? reinterpret_cast<const float4*>(p.pre_o + row * n_pre * D) : nullptr;
   float2 r[kWaveHeld];
@@ -245,8 +250,8 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(const MergeParams 
 
 template <int D>
 hipError_t launch_d(const MergeParams& p, hipStream_t stream) {
-  // records per row are at most n_part (+ the prefix records)
-  if (p.n_part + (p.pre_ml ? p.n_pre : 0) <= kWaveHeld * (256 / D)) {
+  // records per row are at most rec_stride (+ the prefix records)
+  if (p.rec_stride + (p.pre_ml ? p.n_pre : 0) <= kWaveHeld * (256 / D)) {
     const long long rows = (long long)p.batch * p.q_heads;
     const unsigned groups = (unsigned)((rows + kRowsPerGroup - 1) / kRowsPerGroup);
     hipLaunchKernelGGL(merge_wave_kernel<D>, dim3(groups), dim3(kThreads), 0, stream, p);

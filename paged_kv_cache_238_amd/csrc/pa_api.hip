@@ -10,12 +10,11 @@ namespace {
 
 using pa::kBlockTokens;
 
-// Split granularity of both decode kernels (tokens).  A wave streams a run
-// of consecutive partitions, sized on the device from the actual lengths
-// (run_span.h), so the partition only sets the finest split.
+// Finest split of both decode kernels (tokens).  The waves stream balanced
+// chunks of blocks sized on the device from the actual lengths
+// (work_split.h), at least one partition long.
 constexpr int kRunPartition = 256;
-// Runs are lengthened while at least this many remain over the batch
-// (256 CUs x 8 waves).
+// Waves a decode launch aims at (256 CUs x 8 waves).
 #ifndef PA_TARGET_WAVES
 #define PA_TARGET_WAVES 2048
 #endif
@@ -47,7 +46,7 @@ int check_decode_shapes(int max_blocks, int max_context_len, int batch, int q_he
 // Library's partition size: the caller's if given.  Otherwise, when the
 // (sequence, kv head) pairs alone reach the wave target, one
 // partition covering the longest context (no split, no merge); else
-// kRunPartition, with runs sized on the device.
+// kRunPartition, with balanced chunks sized on the device.
 int resolve_partition(int batch, int kv_heads, int max_context_len, int partition_size) {
   if (partition_size > 0) return partition_size;
   if ((long long)batch * kv_heads >= PA_TARGET_WAVES) {
@@ -62,20 +61,29 @@ int num_partitions(int max_context_len, int P) {
   return n > 0 ? n : 1;
 }
 
-// Workspace: [header, 256 B: int32 run span][(m, l) records][o records].
+// Workspace: [header: int32 record mode, then per-sequence record counts
+// from int kCountsAt on; 256-byte aligned][(m, l) records][o records], with
+// n_part + 1 records per (sequence, query head) row: a balanced chunk may
+// start inside a sequence's first partition, so a sequence can span one
+// record more than it has partitions.
 struct Records {
   size_t ml_offset, o_offset, total;
+  int stride;   // records per row
 };
-
-constexpr size_t kHeaderBytes = 256;
 
 Records record_layout(int batch, int q_heads, int head_dim, int n_part) {
   Records r;
-  const size_t n = (size_t)batch * q_heads * n_part;
-  r.ml_offset = kHeaderBytes;
+  r.stride = n_part + 1;
+  const size_t n = (size_t)batch * q_heads * r.stride;
+  r.ml_offset = align_up((pa::kCountsAt + (size_t)batch) * sizeof(int), 256);
   r.o_offset = align_up(r.ml_offset + n * sizeof(float2), 256);
   r.total = r.o_offset + n * head_dim * sizeof(float);
   return r;
+}
+
+// Flattened block count of a batch must fit the kernels' int arithmetic.
+bool blocks_fit(int batch, int max_context_len) {
+  return (long long)batch * ((max_context_len + kBlockTokens - 1) / kBlockTokens) <= INT_MAX;
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -96,7 +104,8 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   if (st != PA_OK) return st;
   const int P = resolve_partition(batch, kv_heads, max_context_len, partition_size);
   const int n_part = num_partitions(max_context_len, P);
-  if ((long long)n_part * batch * kv_heads > INT_MAX) return PA_ERR_SHAPE;   // 1-D grids
+  if ((long long)n_part * batch * kv_heads > INT_MAX || !blocks_fit(batch, max_context_len))
+    return PA_ERR_SHAPE;                     // 1-D grids, flattened block indices
   const bool direct = (mode == 0 && n_part == 1);
   const Records rec = record_layout(batch, q_heads, head_dim, n_part);
   if (!direct) {
@@ -129,6 +138,7 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   p.num_blocks = num_blocks;
   p.partition_size = P;
   p.n_part = n_part;
+  p.rec_stride = rec.stride;
   p.scale_log2 = scale * kLog2e;
   p.direct = direct ? 1 : 0;
   p.target_waves = PA_TARGET_WAVES;
@@ -147,7 +157,7 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   mp.q_heads = q_heads;
   mp.head_dim = head_dim;
   mp.partition_size = P;
-  mp.n_part = n_part;
+  mp.rec_stride = rec.stride;
   mp.max_context_len = max_context_len;
   return status_of(pa::launch_merge(mp, s));
 }
@@ -227,7 +237,7 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   const long long queries = (long long)batch * (q_heads / kv_heads);
   const int tiles = (int)((queries + 15) / 16);
   if ((long long)n_suf * batch * kv_heads > INT_MAX ||
-      (long long)tiles * n_pre * kv_heads > INT_MAX)
+      (long long)tiles * n_pre * kv_heads > INT_MAX || !blocks_fit(batch, suf_max))
     return PA_ERR_SHAPE;
   const PrefixRecords rec = prefix_layout(batch, q_heads, head_dim, n_suf, n_pre);
   if (!workspace) return PA_ERR_NULL;
@@ -254,7 +264,7 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   p.target_waves = PA_TARGET_WAVES;
   p.bt_stride = max_blocks;
 
-  // Suffixes [prefix_len, L_b): run records, as pa_decode_partials would
+  // Suffixes [prefix_len, L_b): records as pa_decode_partials would
   // write them for the shifted sequences.
   pa::DecodeParams ps = p;
   ps.header = reinterpret_cast<int*>(ws);
@@ -264,6 +274,7 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   ps.max_blocks = max_blocks - prefix_len / kBlockTokens;
   ps.max_context_len = suf_max;
   ps.n_part = n_suf;
+  ps.rec_stride = rec.suf.stride;
   st = status_of(pa::launch_decode(ps, kv, s));
   if (st != PA_OK) return st;
 
@@ -275,6 +286,7 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   pp.max_context_len = prefix_len;
   pp.partition_size = P_pre;
   pp.n_part = n_pre;
+  pp.rec_stride = n_pre;
   pp.prefix_tiles = tiles;
   st = status_of(pa::launch_prefix_mfma(pp, kv, s));
   if (st != PA_OK) return st;
@@ -290,7 +302,7 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   mp.q_heads = q_heads;
   mp.head_dim = head_dim;
   mp.partition_size = P;
-  mp.n_part = n_suf;
+  mp.rec_stride = rec.suf.stride;
   mp.max_context_len = suf_max;
   mp.token_offset = prefix_len;
   mp.pre_ml = pp.part_ml;
@@ -587,7 +599,7 @@ int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,
   mp.q_heads = q_heads;
   mp.head_dim = head_dim;
   mp.partition_size = partition_size;
-  mp.n_part = n_part;
+  mp.rec_stride = rec.stride;
   mp.max_context_len = max_context_len;
   return status_of(pa::launch_merge(mp, static_cast<hipStream_t>(stream)));
 }

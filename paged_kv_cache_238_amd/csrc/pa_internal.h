@@ -10,6 +10,12 @@ namespace pa {
 
 constexpr int kBlockTokens = 16;   // tokens per physical KV block
 
+// Workspace header (int32): [0] = record mode (1: record r of a row covers
+// partition r; 0: balanced chunks, per-sequence record counts from
+// header[kCountsAt + b]).  The header takes 256 bytes plus the counts,
+// rounded up to 256 bytes.
+constexpr int kCountsAt = 64;
+
 // KV cache element formats.  The 8-bit ones carry fp32 scales per (token,
 // kv head), laid out [num_blocks, kv_heads, 16].
 enum : int {
@@ -29,8 +35,8 @@ struct DecodeParams {
   const int32_t* context_lens;// [B]
   uint16_t* out;              // fp16 [B, Hq, D]  (direct mode)
   float* lse;                 // fp32 [B, Hq] or null (direct mode)
-  float2* part_ml;            // [B, Hq, n_part] (split mode)
-  float* part_o;              // [B, Hq, n_part, D] (split mode)
+  float2* part_ml;            // [B, Hq, rec_stride] (split mode)
+  float* part_o;              // [B, Hq, rec_stride, D] (split mode)
   int max_blocks;             // table entries per row from token_offset on
   int bt_stride;              // table row stride (entries)
   int token_offset;           // tokens [0, token_offset) of every sequence are
@@ -40,10 +46,11 @@ struct DecodeParams {
   int batch, q_heads, kv_heads, head_dim, num_blocks;
   int partition_size;         // tokens, multiple of 16
   int n_part;                 // ceil(max_context_len / partition_size)
+  int rec_stride;             // records per (sequence, query head) row: n_part + 1
   float scale_log2;           // scale * log2(e)
   int direct;                 // 1: n_part == 1, write out/lse directly
-  int target_waves;           // run-length target (locate_run, run_span.h)
-  int* header;                // split mode: workspace header; [0] = run span
+  int target_waves;           // waves a launch aims at (locate_work, work_split.h)
+  int* header;                // split mode: workspace header (kCountsAt)
   // Shared-prefix mode (matrix-core kernel): the stream is table row 0 over
   // max_context_len tokens (the prefix), one partition per run, and the 16
   // query slots of a wave are queries of different sequences: query
@@ -52,14 +59,14 @@ struct DecodeParams {
 };
 
 struct MergeParams {
-  const int* header;          // [0] = partitions per record (run span)
+  const int* header;          // record mode and per-sequence counts (kCountsAt)
   const float2* part_ml;
   const float* part_o;
   const int32_t* context_lens;
   uint16_t* out;
   float* lse;
   int batch, q_heads, head_dim;
-  int partition_size, n_part, max_context_len;
+  int partition_size, rec_stride, max_context_len;
   int token_offset;           // records cover tokens [token_offset, L)
   // Optional second record set (shared prefix): n_pre records per row, all
   // present.  Null when absent.
@@ -92,17 +99,18 @@ struct CopyParams {
 };
 
 // Workgroups of a decode launch with `wpg` kv heads per workgroup: one per
-// sequence in direct mode; otherwise the number of (run, head group)
-// items, bounded on the host (locate_run in run_span.h): at most
-// n_part * batch * kv_heads / wpg, and at most target_waves / wpg when
-// batch * kv_heads is below the target.
+// sequence in direct mode; n_part * batch partition items when batch *
+// kv_heads reaches the wave target; otherwise at most target_waves /
+// kv_heads balanced chunks (locate_work in work_split.h), and no more than
+// the partitions could fill, each times the head groups.
 inline unsigned decode_workgroups(const DecodeParams& p, int wpg) {
   const long long groups = p.kv_heads / wpg;
   if (p.direct) return (unsigned)(p.batch * groups);
-  const long long full = (long long)p.n_part * p.batch * groups;
-  if ((long long)p.batch * p.kv_heads >= p.target_waves) return (unsigned)full;
-  const long long bound = ((long long)p.target_waves + wpg - 1) / wpg;
-  return (unsigned)(full < bound ? full : bound);
+  const long long full = (long long)p.n_part * p.batch;
+  if ((long long)p.batch * p.kv_heads >= p.target_waves) return (unsigned)(full * groups);
+  long long chunks = p.target_waves / p.kv_heads;
+  if (chunks < 1) chunks = 1;
+  return (unsigned)((full < chunks ? full : chunks) * groups);
 }
 
 // Launchers return hipSuccess or the launch error.  `kv` is the cache

@@ -68,16 +68,27 @@ def test_int8_requires_scales():
     assert st == NULL
 
 
+def _ws_bytes(B, Hq, D, n_part):
+    """Workspace layout: int32 header of 64 words plus one record count per
+    sequence (256-byte aligned), then n_part + 1 records per (sequence,
+    query head): (m, l) float2 records, then 256-byte aligned fp32 o records."""
+    up = lambda x: -(-x // 256) * 256
+    n = B * Hq * (n_part + 1)
+    return up((64 + B) * 4) + up(n * 8) + n * D * 4
+
+
 def test_workspace_and_partition_sizes():
     assert pa.partition_size(4, 64, 8, 128, 131072, 512) == 512
     assert pa.partition_size(4, 64, 8, 128, 131072, 0) % 16 == 0
     assert pa.partition_size(4, 64, 8, 128, 131072, 24) == 0
-    # 256-byte header, then 4 x 64 heads x 256 partitions x (8 B of (m, l)),
-    # then the o records (128 x 4 B each), 256-byte aligned
-    n = 4 * 64 * 256
-    assert pa.workspace_size(4, 64, 8, 128, 131072, 512) == 256 + n * 8 + n * 512
-    n = 4 * 64
-    assert pa.workspace_size(4, 64, 8, 128, 100, 512) == 256 + 2048 + n * 512
+    # 512-byte header (64 + 4 words, rounded up), then 4 x 64 heads x 257
+    # records x (8 B of (m, l)), then the o records (128 x 4 B each)
+    n = 4 * 64 * 257
+    assert pa.workspace_size(4, 64, 8, 128, 131072, 512) == 512 + n * 8 + n * 512
+    assert pa.workspace_size(4, 64, 8, 128, 131072, 512) == _ws_bytes(4, 64, 128, 256)
+    n = 4 * 64 * 2
+    assert pa.workspace_size(4, 64, 8, 128, 100, 512) == 512 + 4096 + n * 512
+    assert pa.workspace_size(4, 64, 8, 64, 100, 512) == _ws_bytes(4, 64, 64, 1)
 
 
 def test_write_validation():
@@ -106,7 +117,7 @@ def test_partition_choice():
     # ... one partition covering the longest context once it reaches 2048
     assert pa.partition_size(64, 32, 32, 128, 1530, 0) == 1536
     assert pa.partition_size(64, 32, 32, 128, 100, 0) == 256
-    assert pa.workspace_size(64, 32, 32, 128, 1530, 0) == 256 + 64 * 32 * (8 + 512)
+    assert pa.workspace_size(64, 32, 32, 128, 1530, 0) == _ws_bytes(64, 32, 128, 1)
 
 
 def spd(**kw):
@@ -129,30 +140,41 @@ def test_shared_prefix_validation(kw, code):
     assert spd(**kw) == code
 
 
+def _sp_bytes(B, Hq, D, n_suf, n_pre):
+    """Shared-prefix workspace: the suffix part laid out like a decode
+    workspace with n_suf partitions, then n_pre prefix records per row
+    ((m, l), then o), each part 256-byte aligned."""
+    up = lambda x: -(-x // 256) * 256
+    rows = B * Hq
+    return up(_ws_bytes(B, Hq, D, n_suf)) + up(rows * n_pre * 8) + rows * n_pre * D * 4
+
+
 def test_shared_prefix_workspace_size():
-    # header; suffix records: a 512-token suffix is 32 blocks, at most eight
-    # partitions of 4 blocks (64 tokens), so 8 of them;
-    # prefix records: 4 query tiles x 32 kv heads = 128 waves per prefix
-    # partition, so 128-token partitions (about 1024 waves), 8 of them;
-    # 256-byte aligned parts
+    # suffix records: a 512-token suffix is 32 blocks, at most eight
+    # partitions of 4 blocks (64 tokens), so 8 of them; prefix records: 4
+    # query tiles x 32 kv heads = 128 waves per prefix partition, so
+    # 128-token partitions (about 1024 waves), 8 of them
     rows = 64 * 32
-    suf = 256 + rows * 8 * 8 + rows * 8 * 512
+    suf = 512 + rows * 9 * 8 + rows * 9 * 512
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
         suf + rows * 8 * 8 + rows * 8 * 512
+    assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
+        _sp_bytes(64, 32, 128, 8, 8)
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1000) == 0
     # longer suffixes: 4096 - 1024 = 3072 tokens, 192 blocks; partitions of
     # 24 blocks would exceed 256 tokens, so 256 (12 partitions); prefix: one
     # query tile x 8 kv heads = 8 waves per partition, so one-block
     # partitions, 64 of them
     assert pa.shared_prefix_workspace_size(8, 8, 8, 128, 4096, 1024) == \
-        256 + 64 * 12 * (8 + 512) + 64 * 64 * (8 + 512)
+        _sp_bytes(8, 8, 128, 12, 64)
+    # no suffix beyond the prefix: one (empty) suffix partition
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1024, 1024) == \
-        256 + rows * (8 + 512) + rows * 8 * (8 + 512)
+        _sp_bytes(64, 32, 128, 1, 8)
     # few queries: 2 tiles x 8 kv heads = 16 waves per partition, so the
     # smallest partition (one block), 64 of them
     assert pa.shared_prefix_workspace_size(4, 64, 8, 128, 1024, 1024) == \
-        256 + 4 * 64 * (8 + 512) + 4 * 64 * 64 * (8 + 512)
+        _sp_bytes(4, 64, 128, 1, 64)
     # many queries: 64 tiles x 32 heads = 2048 waves per partition -> 256 tokens
     # (the largest)
     assert pa.shared_prefix_workspace_size(1024, 32, 32, 64, 1024, 1024) == \
-        256 + 1024 * 32 * (8 + 256) + 1024 * 32 * 4 * (8 + 256)
+        _sp_bytes(1024, 32, 64, 1, 4)

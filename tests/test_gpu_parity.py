@@ -326,6 +326,26 @@ def test_prefix_aliasing_bit_identical_to_private_copies(pa):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def _chunk_records(lens, max_ctx, kv_heads, P, target=2048):
+    """Token ranges of the records the partition kernel writes per sequence
+    when batch * kv_heads is below the wave target: the sequences' blocks laid
+    end to end and cut into chunks of C = max(P/16, ceil(T/K)) blocks, K =
+    target // kv_heads (the record layout pa.h documents)."""
+    nb = [(int(L) + 15) // 16 if 0 < L <= max_ctx else 0 for L in lens]
+    T = sum(nb)
+    C = max(P // 16, -(-T // max(1, target // kv_heads)))
+    out, F = [], 0
+    for b, n in enumerate(nb):
+        recs, c = [], F // C
+        while c * C < F + n:
+            j0, j1 = max(c * C, F) - F, min((c + 1) * C, F + n) - F
+            recs.append((16 * j0, min(16 * j1, int(lens[b]))))
+            c += 1
+        out.append(recs)
+        F += n
+    return out
+
+
 def test_partials_plus_merge_equals_decode(pa):
     wl = gen.make("long128k_int8", small=True)
     vals = gen.fill_numpy(wl, new_slot_poison=False)
@@ -339,21 +359,28 @@ def test_partials_plus_merge_equals_decode(pa):
                            v_scale=d["v_scale"])
     b = pa.merge_partials(ws, d["context_lens"], wl.q_heads, wl.head_dim, P, wl.max_context_len)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    # records against the oracle's own partition statistics (log2 units);
-    # workspace: 256-byte header (int32 partitions per record), then (m, l)
-    n_part = -(-wl.max_context_len // P)
-    span = int(ws[:4].view(torch.int32).item())
-    assert span == 1          # a two-sequence batch keeps one partition per record
-    ml = ws[256:256 + wl.batch * wl.q_heads * n_part * 8].view(torch.float32).view(
-        wl.batch, wl.q_heads, n_part, 2).cpu().numpy()
-    parts = ref.ref_partials(vals["q"], vals["k_pool"], vals["v_pool"], wl.block_table,
-                             wl.context_lens, wl.scale, P, vals["k_scale"], vals["v_scale"])
-    # (m, l) is a reference point and the sum of 2^(s - m) over the
-    # partition: m + log2(l) is the partition's log-sum-exp (log2 units)
-    m, l, _ = parts[1][5]
-    lse_gpu = (ml[1, 5, :len(m), 0] + np.log2(ml[1, 5, :len(m), 1])) * math.log(2)
-    np.testing.assert_allclose(lse_gpu, m + np.log(l), rtol=0, atol=1e-4)
-    assert np.all(ml[1, 5, :len(m), 0] * math.log(2) <= m + 1e-4)
+    # records against the oracle's own statistics over each record's token
+    # range (log2 units).  Workspace: int32 header (record mode 0 = balanced
+    # chunks, record counts from word 64 on), 256-byte aligned; then (m, l)
+    # with n_part + 1 records per row
+    head = ws[:4 * (64 + wl.batch)].view(torch.int32).cpu().numpy()
+    assert head[0] == 0
+    ranges = _chunk_records(wl.context_lens, wl.max_context_len, wl.kv_heads, P)
+    assert list(head[64:64 + wl.batch]) == [len(r) for r in ranges]
+    stride = -(-wl.max_context_len // P) + 1
+    off = -(-(64 + wl.batch) * 4 // 256) * 256
+    ml = ws[off:off + wl.batch * wl.q_heads * stride * 8].view(torch.float32).view(
+        wl.batch, wl.q_heads, stride, 2).cpu().numpy()
+    # block-level statistics from the oracle, combined over each range
+    blocks = ref.ref_partials(vals["q"], vals["k_pool"], vals["v_pool"], wl.block_table,
+                              wl.context_lens, wl.scale, 16, vals["k_scale"], vals["v_scale"])
+    for bb, h in [(0, 0), (1, 5), (wl.batch - 1, wl.q_heads - 1)]:
+        m, l, _ = blocks[bb][h]
+        want = [np.logaddexp.reduce(m[t0 // 16:-(-t1 // 16)] + np.log(l[t0 // 16:-(-t1 // 16)]))
+                for t0, t1 in ranges[bb]]
+        n = len(want)
+        lse_gpu = (ml[bb, h, :n, 0] + np.log2(ml[bb, h, :n, 1])) * math.log(2)
+        np.testing.assert_allclose(lse_gpu, want, rtol=0, atol=1e-4)
 
 
 def test_bad_metadata_gives_nan_rows_not_faults(pa):
@@ -419,10 +446,11 @@ def test_full_size_sampled_rows(pa, name):
     check_close(got, np.stack([want[b, h] for b, h in rows]), f"{name} sampled rows")
 
 
-def test_runs_of_partitions_merged_online(pa):
-    """A long context in a small batch: the matrix-core kernel merges runs of
-    consecutive partitions online (span > 1, read back from the workspace
-    header) and the merge kernel combines the run records."""
+def test_chunks_longer_than_a_partition(pa):
+    """A long context in a small batch with a forced 16-token partition: the
+    balanced chunks are several partitions long (one wave merges them
+    online, the chunk length read back through the record count in the
+    workspace header) and the merge kernel combines the chunk records."""
     over = dict(batch=1, q_heads=8, kv_heads=1, head_dim=64, ctx=70000, scatter=0.15,
                 kv_dtype="fp16", partition_size=16)
     wl = gen.make("long128k_int8", seed=91, overrides=over)
@@ -433,11 +461,12 @@ def test_runs_of_partitions_merged_online(pa):
     out = pa.decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"],
                     scale=wl.scale, partition_size=16, max_context_len=wl.max_context_len,
                     workspace=ws)
-    span = int(ws[:4].view(torch.int32).item())
-    say(f"runs: L={wl.max_context_len} P=16 span={span}")
-    assert span > 1             # 4375 partitions for one (sequence, kv head) pair
+    head = ws[:4 * 65].view(torch.int32).cpu().numpy()
+    say(f"chunks: L={wl.max_context_len} P=16 mode={head[0]} records={head[64]}")
+    # 4375 blocks over at most 2048 chunks: 3 blocks each, 1459 records
+    assert head[0] == 0 and head[64] == 1459
     want, _ = oracle_decode(wl, vals)
-    check_close(out.cpu().numpy(), want, "span-2 runs")
+    check_close(out.cpu().numpy(), want, "three-block chunks")
 
 
 @pytest.mark.parametrize("int8", [False, True])
@@ -479,6 +508,31 @@ def test_runs_enumerated_over_many_sequences(pa, G, int8):
         out, lse = out.cpu().numpy(), lse.cpu().numpy()
         assert not out[~live].any() and np.all(np.isneginf(lse[~live]))
         check_close(out[live], want[live], f"many sequences G={G} int8={int8} P={P}")
+        np.testing.assert_allclose(lse[live], want_lse[live], rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("G,kv", [(1, "fp16"), (2, "fp8"), (8, "fp16"), (8, "int8")])
+def test_chunks_spanning_many_sequences(pa, G, kv):
+    """Many one-block sequences (with empty ones between them): each balanced
+    chunk of 16 blocks crosses up to 16 sequence boundaries, so one wave
+    streams many short segments and writes a record for each, and a
+    sequence's blocks may sit in two chunks."""
+    over = dict(batch=600, q_heads=G * 2, kv_heads=2, head_dim=128, lmin=1, lmax=40,
+                occupancy=0.9, kv_dtype=kv)
+    wl = gen.make("gqa70b_mixed", seed=1100 + G + len(kv), overrides=over)
+    wl.context_lens[::7] = np.minimum(wl.context_lens[::7], 16)
+    wl.context_lens[[2, 3, 300, 599]] = 0
+    wl = _rebuild_table(wl)
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    d = device_inputs(wl, vals)
+    want, want_lse = oracle_decode(wl, vals)
+    live = wl.context_lens > 0
+    for P in (0, 16):
+        say(f"chunks over many sequences G={G} kv={kv} P={P} B={wl.batch}")
+        out, lse = gpu_decode(pa, wl, d, partition_size=P)
+        out, lse = out.cpu().numpy(), lse.cpu().numpy()
+        assert not out[~live].any() and np.all(np.isneginf(lse[~live]))
+        check_close(out[live], want[live], f"chunks over many sequences G={G} kv={kv} P={P}")
         np.testing.assert_allclose(lse[live], want_lse[live], rtol=0, atol=1e-4)
 
 
