@@ -276,12 +276,16 @@ int pa_decode_fp8(void* out, float* lse_out, const void* q, const uint8_t* k_poo
  *                                       2^(s - m); m + log2(l) is the
  *                                       record's log-sum-exp
  *                                       (256-byte aligned after the header)
- *   float  o[batch][q_heads][n_part+1][head_dim]  unnormalised sum 2^(s-m) v
- *                                       (256-byte aligned after ml)
+ *   fp16   u[batch][q_heads][n_part+1][head_dim]  normalised output of the
+ *                                       record, sum 2^(s-m) v / l, rounded
+ *                                       to nearest even (a convex
+ *                                       combination of V rows, so within
+ *                                       V's range); 256-byte aligned after ml
  * Records past a row's count are not written.
  *
- * pa_merge_partials: out[b,h] = sum_r 2^(m_r - M) o_r / sum_r 2^(m_r - M) l_r
- * over the row's records, M = max m_r; lse = ln 2 * (M + log2(den)).
+ * pa_merge_partials: out[b,h] = sum_r w_r u_r / sum_r w_r with
+ * w_r = 2^(m_r - M) l_r over the row's records, M = max m_r, accumulated in
+ * fp32; lse = ln 2 * (M + log2(sum_r w_r)).
  */
 int pa_decode_partials(const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, int max_blocks,

@@ -392,13 +392,18 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
           *reinterpret_cast<uint4*>(p.out + row * D + c * 8) = pk;
           if (c == 0 && p.lse) p.lse[row] = (M + log2f(den)) * kLn2;
         } else {
+          // o / l in fp16 (a convex combination of V rows, so within V's
+          // range); (m, l) stay fp32.
           const size_t rec = row * p.rec_stride + ridx;
-          float4* dst = reinterpret_cast<float4*>(p.part_o + rec * D + c * 8);
-          float4 a = make_float4(o[0], o[1], o[2], o[3]);
-          float4 bq = make_float4(o[4], o[5], o[6], o[7]);
-          if (bad_blk) a = bq = make_float4(M, M, M, M);
-          dst[0] = a;
-          dst[1] = bq;
+          const float inv = 1.0f / den;
+          uint4 pk;
+          uint32_t* pw = reinterpret_cast<uint32_t*>(&pk);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pw[e] = (uint32_t)f32_to_f16_bits(o[2 * e] * inv) |
+                    ((uint32_t)f32_to_f16_bits(o[2 * e + 1] * inv) << 16);
+          if (bad_blk) pk = make_uint4(0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u);
+          *reinterpret_cast<uint4*>(p.part_o + rec * D + c * 8) = pk;
           if (c == 0) p.part_ml[rec] = make_float2(M, den);
         }
       }

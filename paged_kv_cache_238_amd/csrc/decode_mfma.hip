@@ -501,7 +501,7 @@ void decode_mfma_kernel(const DecodeParams p) {
     }
   };
 
-  // Record of the segment (relative to m_run).
+  // Record of the segment: (m_run, l) and the normalised output.
   // Lane (lg, li) holds O[head li][dim 16n + 4lg + i].
   auto finalize = [&]() {
     float den = l_run;
@@ -524,12 +524,19 @@ void decode_mfma_kernel(const DecodeParams p) {
         }
         if (lg == 0 && p.lse) p.lse[row] = (M + log2f(den)) * kLn2;
       } else {
+        // o / l in fp16 (a convex combination of V rows, so within V's
+        // range); (m, l) stay fp32.
         const size_t rec = row * p.rec_stride + ridx;
+        const float inv = 1.0f / den;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          f4 o = acc[n];
-          if (bad_blk) o = f4{M, M, M, M};
-          *reinterpret_cast<f4*>(p.part_o + rec * D + 16 * n + 4 * lg) = o;
+          uint2 o;
+          o.x = (uint32_t)f32_to_f16_bits(acc[n][0] * inv) |
+                ((uint32_t)f32_to_f16_bits(acc[n][1] * inv) << 16);
+          o.y = (uint32_t)f32_to_f16_bits(acc[n][2] * inv) |
+                ((uint32_t)f32_to_f16_bits(acc[n][3] * inv) << 16);
+          if (bad_blk) o = make_uint2(0x7E007E00u, 0x7E007E00u);
+          *reinterpret_cast<uint2*>(p.part_o + rec * D + 16 * n + 4 * lg) = o;
         }
         if (lg == 0) p.part_ml[rec] = make_float2(M, den);
       }

@@ -1,11 +1,12 @@
 // Log-sum-exp merge of split-K partition records into the final fp16 row.
 //
-// Record r of sequence b, query head h carries (m_r, l_r, o_r) for one
+// Record r of sequence b, query head h carries (m_r, l_r, u_r) for one
 // stretch of its blocks (a partition, or a balanced chunk's share of the
 // sequence, as the workspace header says): a reference point m_r for its
-// scores (log2 units), the sum of 2^(s - m_r) and the unnormalised sum of
-// 2^(s - m_r) v.  With M = max_p m_p and w_p = 2^(m_p - M):
-//   out = sum_p w_p o_p / sum_p w_p l_p,   lse = ln2 * (M + log2 sum_p w_p l_p).
+// scores (log2 units), the sum l_r of 2^(s - m_r), and the normalised
+// output u_r = sum 2^(s - m_r) v / l_r in fp16.  With M = max_r m_r and
+// w_r = 2^(m_r - M) l_r:
+//   out = sum_r w_r u_r / sum_r w_r,   lse = ln2 * (M + log2 sum_r w_r).
 // This is the running-max rescaling of the zskr.cn article's PagedAttention
 // kernel (section "PagedAttention 的 Attention 计算修改") applied once
 // across partitions instead of token by token, followed by that kernel's
@@ -52,6 +53,20 @@ __device__ __forceinline__ int suffix_records(const MergeParams& p, int b, int L
   return (L + p.partition_size - 1) / p.partition_size;
 }
 
+// Adds record (m, l, u) with weight w = 2^(m - M) * l: u holds four fp16
+// values of the record's normalised output, so its unnormalised sum is w * u
+// against the common reference M.
+__device__ __forceinline__ void accumulate(float2 ml, uint2 u, float Mu, float4& acc, float& den) {
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  const float wgt = __builtin_amdgcn_exp2f(ml.x - Mu) * ml.y;
+  const h2v a = __builtin_bit_cast(h2v, u.x), c = __builtin_bit_cast(h2v, u.y);
+  den += wgt;
+  acc.x = fmaf(wgt, (float)a[0], acc.x);
+  acc.y = fmaf(wgt, (float)a[1], acc.y);
+  acc.z = fmaf(wgt, (float)c[0], acc.z);
+  acc.w = fmaf(wgt, (float)c[1], acc.w);
+}
+
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   _Float16 h = (_Float16)x;
   return __builtin_bit_cast(uint16_t, h);
@@ -84,9 +99,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
     return;
   }
   const float2* ml = p.part_ml + row * p.rec_stride;
-  const float4* o = reinterpret_cast<const float4*>(p.part_o + row * p.rec_stride * D);
+  const uint2* o = reinterpret_cast<const uint2*>(p.part_o + row * p.rec_stride * D);
   const float2* ml2 = n_pre ? p.pre_ml + row * n_pre : nullptr;
-  const float4* o2 = n_pre ? reinterpret_cast<const float4*>(p.pre_o + row * n_pre * D) : nullptr;
+  const uint2* o2 = n_pre ? reinterpret_cast<const uint2*>(p.pre_o + row * n_pre * D) : nullptr;
   auto rec_ml = [&](int i) { return i < n_suf ? ml[i] : ml2[i - n_suf]; };
   auto rec_o = [&](int i) {
     return i < n_suf ? o[(size_t)i * COLS + col] : o2[(size_t)(i - n_suf) * COLS + col];
@@ -99,12 +114,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
     // Every record this lane needs (phase ph: records ph, ph + PH, ...) is
     // loaded at once, so the whole merge costs one memory round trip.
     float2 r[kHeld];
-    float4 v[kHeld];
+    uint2 v[kHeld];
 #pragma unroll
     for (int k = 0; k < kHeld; ++k) {
       const int i = ph + k * PH;
       r[k] = make_float2(kNegInf, 0.f);
-      v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      v[k] = make_uint2(0, 0);
       if (i < n) {
         r[k] = rec_ml(i);
         v[k] = rec_o(i);
@@ -116,29 +131,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
     const float Mu = (M == kNegInf) ? 0.f : M;
 #pragma unroll
     for (int k = 0; k < kHeld; ++k) {
-      if (ph + k * PH < n) {
-        const float wgt = __builtin_amdgcn_exp2f(r[k].x - Mu);
-        den = fmaf(wgt, r[k].y, den);
-        acc.x = fmaf(wgt, v[k].x, acc.x);
-        acc.y = fmaf(wgt, v[k].y, acc.y);
-        acc.z = fmaf(wgt, v[k].z, acc.z);
-        acc.w = fmaf(wgt, v[k].w, acc.w);
-      }
+      if (ph + k * PH < n) accumulate(r[k], v[k], Mu, acc, den);
     }
   } else {
     for (int i = tid; i < n; i += kThreads) M = fmaxf(M, rec_ml(i).x);
     M = block_max(M, s_max);
     const float Mu = (M == kNegInf) ? 0.f : M;
-    for (int i = ph; i < n; i += PH) {
-      const float2 r = rec_ml(i);
-      const float wgt = __builtin_amdgcn_exp2f(r.x - Mu);
-      den = fmaf(wgt, r.y, den);
-      const float4 v = rec_o(i);
-      acc.x = fmaf(wgt, v.x, acc.x);
-      acc.y = fmaf(wgt, v.y, acc.y);
-      acc.z = fmaf(wgt, v.z, acc.z);
-      acc.w = fmaf(wgt, v.w, acc.w);
-    }
+    for (int i = ph; i < n; i += PH) accumulate(rec_ml(i), rec_o(i), Mu, acc, den);
   }
   s_acc[ph][col] = acc;
   if (col == 0) s_den[ph] = den;
@@ -192,16 +191,16 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(const MergeParams 
     return;
   }
   const float2* ml = p.part_ml + row * p.rec_stride;
-  const float4* o = reinterpret_cast<const float4*>(p.part_o + row * p.rec_stride * D);
+  const uint2* o = reinterpret_cast<const uint2*>(p.part_o + row * p.rec_stride * D);
   const float2* ml2 = n_pre ? p.pre_ml + row * n_pre : nullptr;
-  const float4* o2 = n_pre ? reinterpret_cast<const float4*>(p.pre_o + row * n_pre * D) : nullptr;
+  const uint2* o2 = n_pre ? reinterpret_cast<const uint2*>(p.pre_o + row * n_pre * D) : nullptr;
   float2 r[kWaveHeld];
-  float4 v[kWaveHeld];
+  uint2 v[kWaveHeld];
 #pragma unroll
   for (int k = 0; k < kWaveHeld; ++k) {
     const int i = ph + k * PH;
     r[k] = make_float2(kNegInf, 0.f);
-    v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    v[k] = make_uint2(0, 0);
     if (i < n) {
       r[k] = i < n_suf ? ml[i] : ml2[i - n_suf];
       v[k] = i < n_suf ? o[(size_t)i * COLS + col] : o2[(size_t)(i - n_suf) * COLS + col];
@@ -217,14 +216,7 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(const MergeParams 
   float den = 0.f;
 #pragma unroll
   for (int k = 0; k < kWaveHeld; ++k) {
-    if (ph + k * PH < n) {
-      const float wgt = __builtin_amdgcn_exp2f(r[k].x - Mu);
-      den = fmaf(wgt, r[k].y, den);
-      acc.x = fmaf(wgt, v[k].x, acc.x);
-      acc.y = fmaf(wgt, v[k].y, acc.y);
-      acc.z = fmaf(wgt, v[k].z, acc.z);
-      acc.w = fmaf(wgt, v[k].w, acc.w);
-    }
+    if (ph + k * PH < n) accumulate(r[k], v[k], Mu, acc, den);
   }
   // phases in order: lane col of phase q holds its partial sums
   float dsum = 0.f;

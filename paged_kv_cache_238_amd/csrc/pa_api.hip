@@ -18,6 +18,11 @@ constexpr int kRunPartition = 256;
 #ifndef PA_TARGET_WAVES
 #define PA_TARGET_WAVES 2048
 #endif
+// (sequence, kv head) pairs from which the library gives each pair one wave
+// over its whole context (no split, no merge).
+#ifndef PA_DIRECT_PAIRS
+#define PA_DIRECT_PAIRS 2048
+#endif
 constexpr int kMaxPartition = 1 << 18;      // largest partition accepted (tokens)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -49,7 +54,7 @@ int check_decode_shapes(int max_blocks, int max_context_len, int batch, int q_he
 // kRunPartition, with balanced chunks sized on the device.
 int resolve_partition(int batch, int kv_heads, int max_context_len, int partition_size) {
   if (partition_size > 0) return partition_size;
-  if ((long long)batch * kv_heads >= PA_TARGET_WAVES) {
+  if ((long long)batch * kv_heads >= PA_DIRECT_PAIRS) {
     const int whole = (max(max_context_len, 1) + kBlockTokens - 1) / kBlockTokens * kBlockTokens;
     if (whole <= kMaxPartition) return max(whole, kRunPartition);
   }
@@ -62,7 +67,7 @@ int num_partitions(int max_context_len, int P) {
 }
 
 // Workspace: [header: int32 record mode, then per-sequence record counts
-// from int kCountsAt on; 256-byte aligned][(m, l) records][o records], with
+// from int kCountsAt on; 256-byte aligned][(m, l) records][fp16 o records], with
 // n_part + 1 records per (sequence, query head) row: a balanced chunk may
 // start inside a sequence's first partition, so a sequence can span one
 // record more than it has partitions.
@@ -77,7 +82,7 @@ Records record_layout(int batch, int q_heads, int head_dim, int n_part) {
   const size_t n = (size_t)batch * q_heads * r.stride;
   r.ml_offset = align_up((pa::kCountsAt + (size_t)batch) * sizeof(int), 256);
   r.o_offset = align_up(r.ml_offset + n * sizeof(float2), 256);
-  r.total = r.o_offset + n * head_dim * sizeof(float);
+  r.total = r.o_offset + n * head_dim * sizeof(uint16_t);
   return r;
 }
 
@@ -127,7 +132,7 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
   char* ws = static_cast<char*>(workspace);
   p.header = direct ? nullptr : reinterpret_cast<int*>(ws);
   p.part_ml = direct ? nullptr : reinterpret_cast<float2*>(ws + rec.ml_offset);
-  p.part_o = direct ? nullptr : reinterpret_cast<float*>(ws + rec.o_offset);
+  p.part_o = direct ? nullptr : reinterpret_cast<uint16_t*>(ws + rec.o_offset);
   p.max_blocks = max_blocks;
   p.bt_stride = max_blocks;
   p.max_context_len = max_context_len;
@@ -175,7 +180,7 @@ PrefixRecords prefix_layout(int batch, int q_heads, int head_dim, int n_suf, int
   const size_t n = (size_t)batch * q_heads * n_pre;
   r.pre_ml = align_up(r.suf.total, 256);
   r.pre_o = align_up(r.pre_ml + n * sizeof(float2), 256);
-  r.total = r.pre_o + n * head_dim * sizeof(float);
+  r.total = r.pre_o + n * head_dim * sizeof(uint16_t);
   return r;
 }
 
@@ -269,7 +274,7 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   pa::DecodeParams ps = p;
   ps.header = reinterpret_cast<int*>(ws);
   ps.part_ml = reinterpret_cast<float2*>(ws + rec.suf.ml_offset);
-  ps.part_o = reinterpret_cast<float*>(ws + rec.suf.o_offset);
+  ps.part_o = reinterpret_cast<uint16_t*>(ws + rec.suf.o_offset);
   ps.token_offset = prefix_len;
   ps.max_blocks = max_blocks - prefix_len / kBlockTokens;
   ps.max_context_len = suf_max;
@@ -281,7 +286,7 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   // Prefix: one record per (sequence, query head, prefix partition).
   pa::DecodeParams pp = p;
   pp.part_ml = reinterpret_cast<float2*>(ws + rec.pre_ml);
-  pp.part_o = reinterpret_cast<float*>(ws + rec.pre_o);
+  pp.part_o = reinterpret_cast<uint16_t*>(ws + rec.pre_o);
   pp.max_blocks = prefix_len / kBlockTokens;
   pp.max_context_len = prefix_len;
   pp.partition_size = P_pre;
@@ -591,7 +596,7 @@ int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,
   const char* ws = static_cast<const char*>(workspace);
   mp.header = reinterpret_cast<const int*>(ws);
   mp.part_ml = reinterpret_cast<const float2*>(ws + rec.ml_offset);
-  mp.part_o = reinterpret_cast<const float*>(ws + rec.o_offset);
+  mp.part_o = reinterpret_cast<const uint16_t*>(ws + rec.o_offset);
   mp.context_lens = context_lens;
   mp.out = static_cast<uint16_t*>(out);
   mp.lse = lse_out;

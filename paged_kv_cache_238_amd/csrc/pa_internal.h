@@ -36,7 +36,7 @@ struct DecodeParams {
   uint16_t* out;              // fp16 [B, Hq, D]  (direct mode)
   float* lse;                 // fp32 [B, Hq] or null (direct mode)
   float2* part_ml;            // [B, Hq, rec_stride] (split mode)
-  float* part_o;              // [B, Hq, rec_stride, D] (split mode)
+  uint16_t* part_o;           // fp16 [B, Hq, rec_stride, D], normalised (split mode)
   int max_blocks;             // table entries per row from token_offset on
   int bt_stride;              // table row stride (entries)
   int token_offset;           // tokens [0, token_offset) of every sequence are
@@ -61,7 +61,7 @@ struct DecodeParams {
 struct MergeParams {
   const int* header;          // record mode and per-sequence counts (kCountsAt)
   const float2* part_ml;
-  const float* part_o;
+  const uint16_t* part_o;     // fp16 normalised outputs
   const int32_t* context_lens;
   uint16_t* out;
   float* lse;
@@ -71,7 +71,7 @@ struct MergeParams {
   // Optional second record set (shared prefix): n_pre records per row, all
   // present.  Null when absent.
   const float2* pre_ml;
-  const float* pre_o;
+  const uint16_t* pre_o;
   int n_pre;
 };
 

@@ -71,10 +71,10 @@ def test_int8_requires_scales():
 def _ws_bytes(B, Hq, D, n_part):
     """Workspace layout: int32 header of 64 words plus one record count per
     sequence (256-byte aligned), then n_part + 1 records per (sequence,
-    query head): (m, l) float2 records, then 256-byte aligned fp32 o records."""
+    query head): (m, l) float2 records, then 256-byte aligned fp16 o records."""
     up = lambda x: -(-x // 256) * 256
     n = B * Hq * (n_part + 1)
-    return up((64 + B) * 4) + up(n * 8) + n * D * 4
+    return up((64 + B) * 4) + up(n * 8) + n * D * 2
 
 
 def test_workspace_and_partition_sizes():
@@ -82,12 +82,12 @@ def test_workspace_and_partition_sizes():
     assert pa.partition_size(4, 64, 8, 128, 131072, 0) % 16 == 0
     assert pa.partition_size(4, 64, 8, 128, 131072, 24) == 0
     # 512-byte header (64 + 4 words, rounded up), then 4 x 64 heads x 257
-    # records x (8 B of (m, l)), then the o records (128 x 4 B each)
+    # records x (8 B of (m, l)), then the o records (128 x 2 B each)
     n = 4 * 64 * 257
-    assert pa.workspace_size(4, 64, 8, 128, 131072, 512) == 512 + n * 8 + n * 512
+    assert pa.workspace_size(4, 64, 8, 128, 131072, 512) == 512 + n * 8 + n * 256
     assert pa.workspace_size(4, 64, 8, 128, 131072, 512) == _ws_bytes(4, 64, 128, 256)
     n = 4 * 64 * 2
-    assert pa.workspace_size(4, 64, 8, 128, 100, 512) == 512 + 4096 + n * 512
+    assert pa.workspace_size(4, 64, 8, 128, 100, 512) == 512 + 4096 + n * 256
     assert pa.workspace_size(4, 64, 8, 64, 100, 512) == _ws_bytes(4, 64, 64, 1)
 
 
@@ -146,7 +146,7 @@ def _sp_bytes(B, Hq, D, n_suf, n_pre):
     ((m, l), then o), each part 256-byte aligned."""
     up = lambda x: -(-x // 256) * 256
     rows = B * Hq
-    return up(_ws_bytes(B, Hq, D, n_suf)) + up(rows * n_pre * 8) + rows * n_pre * D * 4
+    return up(_ws_bytes(B, Hq, D, n_suf)) + up(rows * n_pre * 8) + rows * n_pre * D * 2
 
 
 def test_shared_prefix_workspace_size():
@@ -155,9 +155,9 @@ def test_shared_prefix_workspace_size():
     # query tiles x 32 kv heads = 128 waves per prefix partition, so
     # 128-token partitions (about 1024 waves), 8 of them
     rows = 64 * 32
-    suf = 512 + rows * 9 * 8 + rows * 9 * 512
+    suf = 512 + rows * 9 * 8 + rows * 9 * 256
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
-        suf + rows * 8 * 8 + rows * 8 * 512
+        suf + rows * 8 * 8 + rows * 8 * 256
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
         _sp_bytes(64, 32, 128, 8, 8)
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1000) == 0
