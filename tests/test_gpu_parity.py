@@ -597,3 +597,47 @@ def test_run_longer_than_lds_id_buffer(pa, kv):
     want, want_lse = oracle_decode(wl, vals)
     check_close(out.cpu().numpy(), want, f"id refill kv={kv}")
     np.testing.assert_allclose(lse.cpu().numpy(), want_lse, rtol=0, atol=1e-4)
+
+
+def _random_case(i):
+    """Seeded shape draw for the randomized sweep: batch, heads, group,
+    head_dim, cache format, length range, forced partition, and a few empty
+    sequences."""
+    rng = np.random.default_rng(5000 + i)
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 161 if Hkv <= 2 else 41))
+    D = int(rng.choice([64, 128]))
+    kv = str(rng.choice(["fp16", "int8", "fp8"]))
+    lmax = int(rng.choice([16, 40, 300, 1500, 2600]))
+    P = int(rng.choice([0, 16, 48, 256]))
+    if rng.random() < 0.2:               # (sequence, kv head) pairs past 2048 waves
+        B, Hkv, lmax = int(rng.integers(1024, 1300)), 2, int(rng.choice([16, 300]))
+    over = dict(batch=B, q_heads=G * Hkv, kv_heads=Hkv, head_dim=D, lmin=1, lmax=lmax,
+                occupancy=0.9, kv_dtype=kv)
+    wl = gen.make("gqa70b_mixed", seed=6000 + i, overrides=over)
+    empty = rng.random(B) < 0.1
+    wl.context_lens[empty] = 0
+    if not wl.context_lens.any():
+        wl.context_lens[0] = 1
+    return _rebuild_table(wl), P
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_randomized_shapes(pa, i):
+    """Seeded sweep over batch, group, kv heads, head_dim, cache format,
+    length range and partition: every configuration of the work split
+    (balanced chunks crossing sequences, partition items, direct) against
+    the oracle, empty sequences included."""
+    wl, P = _random_case(i)
+    say(f"random {i}: B={wl.batch} Hq={wl.q_heads} Hkv={wl.kv_heads} D={wl.head_dim} "
+        f"kv={wl.kv_dtype} max_ctx={wl.max_context_len} P={P}")
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    d = device_inputs(wl, vals)
+    want, want_lse = oracle_decode(wl, vals)
+    out, lse = gpu_decode(pa, wl, d, partition_size=P)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    live = wl.context_lens > 0
+    assert not out[~live].any() and np.all(np.isneginf(lse[~live]))
+    check_close(out[live], want[live], f"random {i}")
+    np.testing.assert_allclose(lse[live], want_lse[live], rtol=0, atol=1e-4)
