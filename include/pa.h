@@ -235,6 +235,59 @@ int pa_decode_fp8(void* out, float* lse_out, const void* q, const uint8_t* k_poo
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step with the KV write folded in: writes each sequence's new
+ * token (k_new / v_new, fp16 [batch, kv_heads, head_dim], the token at
+ * position L_b - 1, L_b = context_lens[b] including it) into the slot the
+ * block table gives for that position - copied for fp16 caches, quantised
+ * per (token, kv head) row for int8 and FP8 exactly as pa_write_kv_int8 /
+ * pa_write_kv_fp8 do - and computes out / lse_out as pa_decode would
+ * afterwards.  Equivalent to pa_write_kv* with slot_mapping[b] =
+ * block_table[b][(L_b - 1) / 16] * 16 + (L_b - 1) % 16, then pa_decode*
+ * (WriteKV then page-table attention, [ATB-PA] "踩坑三" and "PagedAttention
+ * 的 Attention 计算修改").  Two launches on `stream`: the partition kernel
+ * over tokens [0, L_b - 1), whose extra workgroups do the write and the new
+ * token's (max, sum, output) record, then the log-sum-exp merge of both
+ * record sets; the write thus overlaps the attention instead of preceding
+ * it.  The split is always taken (never the one-launch direct path).
+ *   workspace  >= pa_decode_append_workspace_size(...) bytes: the
+ *              pa_decode_partials layout, then 256-byte aligned float2
+ *              (m, l) [batch][q_heads] and fp16 u [batch][q_heads][head_dim]
+ *              for the new tokens
+ *   k_scale / v_scale (8-bit caches)  fp32 [num_blocks, kv_heads, 16],
+ *              read and written
+ * L_b = 0 gives a zero row and writes nothing for b; L_b outside
+ * [0, max_context_len] gives a NaN row; a table entry for position L_b - 1
+ * outside the pool skips b's write and gives NaN rows.  Other arguments,
+ * status codes and caller contracts as pa_decode; additionally each new
+ * token's slot must lie in a block no other sequence of the call uses.
+ */
+size_t pa_decode_append_workspace_size(int batch, int q_heads, int kv_heads, int head_dim,
+                                       int max_context_len, int partition_size);
+
+int pa_decode_append(void* out, float* lse_out, const void* q, const void* k_new,
+                     const void* v_new, void* k_pool, void* v_pool, const int32_t* block_table,
+                     int max_blocks, const int32_t* context_lens, int max_context_len, int batch,
+                     int q_heads, int kv_heads, int head_dim, int block_size, int num_blocks,
+                     float scale, int partition_size, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+int pa_decode_append_int8(void* out, float* lse_out, const void* q, const void* k_new,
+                          const void* v_new, int8_t* k_pool, int8_t* v_pool, float* k_scale,
+                          float* v_scale, const int32_t* block_table, int max_blocks,
+                          const int32_t* context_lens, int max_context_len, int batch,
+                          int q_heads, int kv_heads, int head_dim, int block_size,
+                          int num_blocks, float scale, int partition_size, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+int pa_decode_append_fp8(void* out, float* lse_out, const void* q, const void* k_new,
+                         const void* v_new, uint8_t* k_pool, uint8_t* v_pool, float* k_scale,
+                         float* v_scale, const int32_t* block_table, int max_blocks,
+                         const int32_t* context_lens, int max_context_len, int batch,
+                         int q_heads, int kv_heads, int head_dim, int block_size,
+                         int num_blocks, float scale, int partition_size, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * The two stages pa_decode runs, exported for callers that combine
  * partial results from several sources (for example one sequence's
  * context split across devices, or a shared prefix attended once and

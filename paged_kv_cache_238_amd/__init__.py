@@ -32,7 +32,7 @@ __all__ = [
     "write_kv_fp8", "partition_size", "workspace_size", "decode", "decode_int8",
     "decode_fp8", "copy_blocks", "decode_partials",
     "decode_partials_int8", "merge_partials", "decode_shared_prefix",
-    "shared_prefix_workspace_size", "EXPORTS",
+    "shared_prefix_workspace_size", "decode_append", "append_workspace_size", "EXPORTS",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +78,13 @@ EXPORTS = {
     "pa_decode_partials_fp8": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
                                     _i, _f, _i, _p, _z, _p]),
     "pa_merge_partials": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _z, _p]),
+    "pa_decode_append_workspace_size": (_z, [_i, _i, _i, _i, _i, _i]),
+    "pa_decode_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
+                              _i, _f, _i, _p, _z, _p]),
+    "pa_decode_append_int8": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i,
+                                   _i, _i, _i, _i, _f, _i, _p, _z, _p]),
+    "pa_decode_append_fp8": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i,
+                                  _i, _i, _i, _i, _f, _i, _p, _z, _p]),
     "pa_decode_shared_prefix_workspace_size": (_z, [_i, _i, _i, _i, _i, _i]),
     "pa_decode_shared_prefix": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
                                      _i, _f, _i, _p, _z, _p]),
@@ -341,6 +348,52 @@ def decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, s
                              _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB, scale,
                              partition_size, _ptr(ws), ws.numel(), _stream(q)),
            "pa_decode_fp8")
+    return (out, lse) if return_lse else out
+
+
+def append_workspace_size(batch, q_heads, kv_heads, head_dim, max_context_len,
+                          partition_size=0) -> int:
+    return int(lib.pa_decode_append_workspace_size(batch, q_heads, kv_heads, head_dim,
+                                                   max_context_len, partition_size))
+
+
+def decode_append(q, k_new, v_new, k_pool, v_pool, block_table, context_lens, scale=None,
+                  partition_size=0, max_context_len=None, out=None, return_lse=False,
+                  workspace=None, k_scale=None, v_scale=None, kv_format=None):
+    """Write each sequence's new token (k_new / v_new [B, Hkv, D] fp16, at
+    position context_lens[b] - 1) into its slot and decode over the whole
+    context, in two launches.  The cache format follows k_pool's dtype
+    (float16, int8, or uint8 codes = FP8 E4M3, which needs kv_format="fp8";
+    8-bit caches need k_scale / v_scale, which the call updates)."""
+    torch = _torch()
+    if kv_format is None:
+        kv_format = {torch.float16: "fp16", torch.int8: "int8"}.get(k_pool.dtype, "fp8")
+    dtype = {"fp16": torch.float16, "int8": torch.int8, "fp8": torch.uint8}[kv_format]
+    if kv_format == "fp8":
+        k_pool, v_pool = _codes(k_pool), _codes(v_pool)
+    B, Hq, Hkv, D, NB, bs, MB, L = _decode_args(q, k_pool, v_pool, block_table, context_lens,
+                                                dtype, max_context_len, k_scale, v_scale)
+    _need(k_new, "k_new", torch.float16, 3, q.device)
+    _need(v_new, "v_new", torch.float16, 3, q.device)
+    if k_new.shape != (B, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("decode_append: k_new / v_new must be [batch, kv_heads, head_dim]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out, lse = _alloc_out(q, out, return_lse)
+    need = append_workspace_size(B, Hq, Hkv, D, L, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small")
+    head = (_ptr(out), _ptr(lse), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool))
+    tail = (_ptr(block_table), MB, _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB, scale,
+            partition_size, _ptr(workspace), workspace.numel(), _stream(q))
+    if kv_format == "fp16":
+        _check(lib.pa_decode_append(*head, *tail), "pa_decode_append")
+    else:
+        if k_scale is None or v_scale is None:
+            raise ValueError("decode_append: 8-bit caches need k_scale and v_scale")
+        fn = lib.pa_decode_append_int8 if kv_format == "int8" else lib.pa_decode_append_fp8
+        _check(fn(*head, _ptr(k_scale), _ptr(v_scale), *tail), "pa_decode_append_" + kv_format)
     return (out, lse) if return_lse else out
 
 

@@ -30,6 +30,7 @@
 // no cross-row traffic; row groups are merged once per segment.  Scores are
 // kept in log2 units (scale * log2 e folded in), so exp is one v_exp_f32.
 #include "pa_internal.h"
+#include "append.h"
 #include "work_split.h"
 
 #include <type_traits>
@@ -145,6 +146,14 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   const int r = lane / LPR, c = lane % LPR;
   const int Hq = p.q_heads, Hkv = p.kv_heads;
 
+  // Append mode: the workgroups past the partition work write the newest
+  // tokens and their records (append.h).
+  if (p.k_new != nullptr && (int)blockIdx.x >= p.main_groups) {
+    const long long pair = (long long)(blockIdx.x - p.main_groups) * wpg + w;
+    if (pair < (long long)p.batch * Hkv) append_token<D, G, KV>(p, (int)pair);
+    return;
+  }
+
   // Workgroup item: a balanced chunk of blocks, a (partition, sequence) or a
   // sequence, with a head group (locate_work).  A chunk may cross sequence
   // boundaries; each sequence it reaches is one segment with its own record.
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   // Start-up loads, independent of each other: the length (unless the
   // search already read it), the first 64 block ids of the segment (clamped
   // to the table row) and Q.
-  const int L = seg_len >= 0 ? seg_len : p.context_lens[b] - p.token_offset;
+  const int L = seg_len >= 0 ? seg_len : seq_len(p, b);
   const int row_left = p.max_blocks - j0;
   // Block ids c0 .. c0+63 of the segment, one per lane, through a buffer
   // resource bounded to the segment's slice of the table row: ids past the
@@ -469,8 +478,10 @@ int waves_per_group(const DecodeParams& p) {
 template <int D, int G, int KV>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   const int wpg = waves_per_group(p);
-  const unsigned grid = decode_workgroups(p, wpg);
-  hipLaunchKernelGGL((decode_valu_kernel<D, G, KV>), dim3(grid), dim3(64 * wpg), 0, stream, p);
+  DecodeParams q = p;
+  q.main_groups = (int)decode_workgroups(p, wpg);
+  const unsigned grid = (unsigned)q.main_groups + append_workgroups(p, wpg);
+  hipLaunchKernelGGL((decode_valu_kernel<D, G, KV>), dim3(grid), dim3(64 * wpg), 0, stream, q);
   return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@
 // staged on chip once per workgroup, section "踩坑一"; query heads grouped on
 // one K/V head, discosf.com article, section "二、优化方向").
 #include "pa_internal.h"
+#include "append.h"
 #include "work_split.h"
 
 #include <type_traits>
@@ -220,6 +221,16 @@ void decode_mfma_kernel(const DecodeParams p) {
   const int li = lane & 15;       // index in group: token row for loads, head for softmax
   const int Hq = p.q_heads, Hkv = p.kv_heads;
 
+  // Append mode: the workgroups past the partition work write the newest
+  // tokens and their records (append.h).
+  if constexpr (!PREFIX) {
+    if (p.k_new != nullptr && (int)blockIdx.x >= p.main_groups) {
+      const long long pair = (long long)(blockIdx.x - p.main_groups) * wpg + w;
+      if (pair < (long long)p.batch * Hkv) append_token<D, G, KV>(p, (int)pair);
+      return;
+    }
+  }
+
   // Workgroup item: a balanced chunk of blocks, a (partition, sequence) or a
   // sequence, with a head group (locate_work); a chunk may cross sequence
   // boundaries, and each sequence it reaches is one segment with its own
@@ -297,7 +308,7 @@ void decode_mfma_kernel(const DecodeParams p) {
   // Start-up loads, independent of each other: the length (unless the
   // search already read it) and Q.
   const int L = PREFIX ? p.max_context_len
-                       : seg_len >= 0 ? seg_len : p.context_lens[b] - p.token_offset;
+                       : seg_len >= 0 ? seg_len : seq_len(p, b);
   const int row_left = p.max_blocks - j0;
   // The segment's slice of the table row as a buffer resource: ids past the
   // slice read as 0 with no branch.
@@ -611,9 +622,11 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   using Geo = Geometry<D, KV != kKvF16>;
   const int wpg = waves_per_group(p);
   const size_t lds = (size_t)wpg * kBlockTokens * Geo::kRowBytes + kIdCap * sizeof(int32_t);
-  const unsigned grid = decode_workgroups(p, wpg);
+  DecodeParams q = p;
+  q.main_groups = (int)decode_workgroups(p, wpg);
+  const unsigned grid = (unsigned)q.main_groups + append_workgroups(p, wpg);
   hipLaunchKernelGGL((decode_mfma_kernel<D, G, KV, false>), dim3(grid), dim3(64 * wpg), lds,
-                     stream, p);
+                     stream, q);
   return hipGetLastError();
 }
 

@@ -22,7 +22,9 @@
 //
 // Shared-prefix decode merges two record sets per row: the records over the
 // private suffix [prefix, L) and n_pre records over the shared prefix;
-// both enter the same sums (the log-sum-exp merge is associative).
+// both enter the same sums (the log-sum-exp merge is associative).  The
+// append path uses the second set for the newest token of each row (one
+// record) and the first for tokens [0, L - 1).
 #include "pa_internal.h"
 
 namespace pa {
@@ -90,8 +92,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
     if (tid == 0 && p.lse) p.lse[row] = __builtin_nanf("");
     return;
   }
-  const int n_suf = suffix_records(p, b, L);
-  const int n_pre = p.pre_ml ? p.n_pre : 0;
+  // Append mode: the row's last token is its own record in the second set;
+  // a sequence with no tokens has neither.
+  const int n_suf = L > 0 ? suffix_records(p, b, L - p.len_trim) : 0;
+  const int n_pre = (p.pre_ml && (L > 0 || !p.len_trim)) ? p.n_pre : 0;
   const int n = n_suf + n_pre;               // records: suffix, then prefix
   if (n == 0) {
     for (int d = tid; d < D; d += kThreads) p.out[row * D + d] = 0;
@@ -182,8 +186,10 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(const MergeParams 
     if (lane == 0 && p.lse) p.lse[row] = __builtin_nanf("");
     return;
   }
-  const int n_suf = suffix_records(p, b, L);
-  const int n_pre = p.pre_ml ? p.n_pre : 0;
+  // Append mode: the row's last token is its own record in the second set;
+  // a sequence with no tokens has neither.
+  const int n_suf = L > 0 ? suffix_records(p, b, L - p.len_trim) : 0;
+  const int n_pre = (p.pre_ml && (L > 0 || !p.len_trim)) ? p.n_pre : 0;
   const int n = n_suf + n_pre;
   if (n == 0) {
     for (int d = lane; d < D; d += 64) p.out[row * D + d] = 0;

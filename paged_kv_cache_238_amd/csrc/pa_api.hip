@@ -316,6 +316,105 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   return status_of(pa::launch_merge(mp, s));
 }
 
+// Append workspace: the decode workspace, then one record per (sequence,
+// query head) for the newest token: (m, l) float2 [B, Hq], fp16 u [B, Hq, D].
+struct AppendRecords {
+  Records part;
+  size_t app_ml, app_o, total;
+};
+
+AppendRecords append_layout(int batch, int q_heads, int head_dim, int n_part) {
+  AppendRecords r;
+  r.part = record_layout(batch, q_heads, head_dim, n_part);
+  const size_t n = (size_t)batch * q_heads;
+  r.app_ml = align_up(r.part.total, 256);
+  r.app_o = align_up(r.app_ml + n * sizeof(float2), 256);
+  r.total = r.app_o + n * head_dim * sizeof(uint16_t);
+  return r;
+}
+
+// Write each sequence's newest token (position context_lens[b] - 1) into its
+// slot and decode over the whole context, in two launches: the partition
+// kernel over tokens [0, L - 1) with the write and the new token's records
+// in extra workgroups of the same grid, then the merge of both record sets.
+int append_common(void* out, float* lse_out, const void* q, const void* k_new, const void* v_new,
+                  void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv,
+                  const int32_t* block_table, int max_blocks, const int32_t* context_lens,
+                  int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
+                  int block_size, int num_blocks, float scale, int partition_size,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out || !q || !k_new || !v_new || !k_pool || !v_pool || !block_table || !context_lens)
+    return PA_ERR_NULL;
+  if (kv != pa::kKvF16 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  int st = check_decode_shapes(max_blocks, max_context_len, batch, q_heads, kv_heads, head_dim,
+                               block_size, num_blocks, partition_size);
+  if (st != PA_OK) return st;
+  const int P = resolve_partition(batch, kv_heads, max_context_len, partition_size);
+  const int n_part = num_partitions(max_context_len, P);
+  if ((long long)n_part * batch * kv_heads > INT_MAX || !blocks_fit(batch, max_context_len))
+    return PA_ERR_SHAPE;
+  const AppendRecords rec = append_layout(batch, q_heads, head_dim, n_part);
+  if (!workspace) return PA_ERR_NULL;
+  if (workspace_bytes < rec.total) return PA_ERR_WORKSPACE;
+  if (batch == 0) return PA_OK;
+
+  char* ws = static_cast<char*>(workspace);
+  pa::DecodeParams p = {};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.k_scale_w = k_scale;
+  p.v_scale_w = v_scale;
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.header = reinterpret_cast<int*>(ws);
+  p.part_ml = reinterpret_cast<float2*>(ws + rec.part.ml_offset);
+  p.part_o = reinterpret_cast<uint16_t*>(ws + rec.part.o_offset);
+  p.app_ml = reinterpret_cast<float2*>(ws + rec.app_ml);
+  p.app_o = reinterpret_cast<uint16_t*>(ws + rec.app_o);
+  p.max_blocks = max_blocks;
+  p.bt_stride = max_blocks;
+  p.max_context_len = max_context_len;
+  p.len_trim = 1;
+  p.batch = batch;
+  p.q_heads = q_heads;
+  p.kv_heads = kv_heads;
+  p.head_dim = head_dim;
+  p.num_blocks = num_blocks;
+  p.partition_size = P;
+  p.n_part = n_part;
+  p.rec_stride = rec.part.stride;
+  p.scale_log2 = scale * kLog2e;
+  p.direct = 0;
+  p.target_waves = PA_TARGET_WAVES;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = status_of(pa::launch_decode(p, kv, s));
+  if (st != PA_OK) return st;
+
+  pa::MergeParams mp = {};
+  mp.header = p.header;
+  mp.part_ml = p.part_ml;
+  mp.part_o = p.part_o;
+  mp.context_lens = context_lens;
+  mp.out = static_cast<uint16_t*>(out);
+  mp.lse = lse_out;
+  mp.batch = batch;
+  mp.q_heads = q_heads;
+  mp.head_dim = head_dim;
+  mp.partition_size = P;
+  mp.rec_stride = rec.part.stride;
+  mp.max_context_len = max_context_len;
+  mp.len_trim = 1;
+  mp.pre_ml = p.app_ml;
+  mp.pre_o = p.app_o;
+  mp.n_pre = 1;
+  return status_of(pa::launch_merge(mp, s));
+}
+
 int check_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                 const void* k_pool, const void* v_pool, int num_tokens, int num_blocks,
                 int block_size, int kv_heads, int head_dim) {
@@ -484,6 +583,52 @@ int pa_decode_fp8(void* out, float* lse_out, const void* q, const uint8_t* k_poo
   return decode_common(0, out, lse_out, q, k_pool, v_pool, k_scale, v_scale, pa::kKvF8,
                        block_table, max_blocks, context_lens, max_context_len, batch, q_heads,
                        kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
+                       workspace, workspace_bytes, stream);
+}
+
+size_t pa_decode_append_workspace_size(int batch, int q_heads, int kv_heads, int head_dim,
+                                       int max_context_len, int partition_size) {
+  const int P = pa_decode_partition_size(batch, q_heads, kv_heads, head_dim, max_context_len,
+                                         partition_size);
+  if (P == 0) return 0;
+  return append_layout(batch, q_heads, head_dim, num_partitions(max_context_len, P)).total;
+}
+
+int pa_decode_append(void* out, float* lse_out, const void* q, const void* k_new,
+                     const void* v_new, void* k_pool, void* v_pool, const int32_t* block_table,
+                     int max_blocks, const int32_t* context_lens, int max_context_len, int batch,
+                     int q_heads, int kv_heads, int head_dim, int block_size, int num_blocks,
+                     float scale, int partition_size, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return append_common(out, lse_out, q, k_new, v_new, k_pool, v_pool, nullptr, nullptr,
+                       pa::kKvF16, block_table, max_blocks, context_lens, max_context_len, batch,
+                       q_heads, kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
+                       workspace, workspace_bytes, stream);
+}
+
+int pa_decode_append_int8(void* out, float* lse_out, const void* q, const void* k_new,
+                          const void* v_new, int8_t* k_pool, int8_t* v_pool, float* k_scale,
+                          float* v_scale, const int32_t* block_table, int max_blocks,
+                          const int32_t* context_lens, int max_context_len, int batch,
+                          int q_heads, int kv_heads, int head_dim, int block_size,
+                          int num_blocks, float scale, int partition_size, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return append_common(out, lse_out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
+                       pa::kKvI8, block_table, max_blocks, context_lens, max_context_len, batch,
+                       q_heads, kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
+                       workspace, workspace_bytes, stream);
+}
+
+int pa_decode_append_fp8(void* out, float* lse_out, const void* q, const void* k_new,
+                         const void* v_new, uint8_t* k_pool, uint8_t* v_pool, float* k_scale,
+                         float* v_scale, const int32_t* block_table, int max_blocks,
+                         const int32_t* context_lens, int max_context_len, int batch,
+                         int q_heads, int kv_heads, int head_dim, int block_size,
+                         int num_blocks, float scale, int partition_size, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return append_common(out, lse_out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
+                       pa::kKvF8, block_table, max_blocks, context_lens, max_context_len, batch,
+                       q_heads, kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
                        workspace, workspace_bytes, stream);
 }
 

@@ -43,6 +43,8 @@ struct DecodeParams {
                               // skipped (multiple of 16): lengths and table rows
                               // are read past them
   int max_context_len;        // bound on context_lens - token_offset
+  int len_trim;               // tokens dropped from the end of every sequence
+                              // (1 when the launch appends the newest token itself)
   int batch, q_heads, kv_heads, head_dim, num_blocks;
   int partition_size;         // tokens, multiple of 16
   int n_part;                 // ceil(max_context_len / partition_size)
@@ -51,6 +53,16 @@ struct DecodeParams {
   int direct;                 // 1: n_part == 1, write out/lse directly
   int target_waves;           // waves a launch aims at (locate_work, work_split.h)
   int* header;                // split mode: workspace header (kCountsAt)
+  // Append mode: workgroups from main_groups on write each sequence's new
+  // token (position context_lens[b] - 1) from k_new / v_new into its slot and
+  // emit that token's record into app_ml / app_o ([B, Hq], one record per row).
+  int main_groups;            // workgroups of the partition work (append mode)
+  const uint16_t* k_new;      // fp16 [B, Hkv, D]
+  const uint16_t* v_new;
+  float* k_scale_w;           // 8-bit pools: the scales the append writes
+  float* v_scale_w;
+  float2* app_ml;
+  uint16_t* app_o;
   // Shared-prefix mode (matrix-core kernel): the stream is table row 0 over
   // max_context_len tokens (the prefix), one partition per run, and the 16
   // query slots of a wave are queries of different sequences: query
@@ -67,7 +79,8 @@ struct MergeParams {
   float* lse;
   int batch, q_heads, head_dim;
   int partition_size, rec_stride, max_context_len;
-  int token_offset;           // records cover tokens [token_offset, L)
+  int token_offset;           // records cover tokens [token_offset, L - len_trim)
+  int len_trim;               // 1: the row's last token is in the second record set
   // Optional second record set (shared prefix): n_pre records per row, all
   // present.  Null when absent.
   const float2* pre_ml;
@@ -98,6 +111,11 @@ struct CopyParams {
   size_t block_bytes;         // 16 * kv_heads * head_dim * element bytes
 };
 
+// Length of sequence b as the partition work sees it.
+__device__ __forceinline__ int seq_len(const DecodeParams& p, int b) {
+  return p.context_lens[b] - p.token_offset - p.len_trim;
+}
+
 // Workgroups of a decode launch with `wpg` kv heads per workgroup: one per
 // sequence in direct mode; n_part * batch partition items when batch *
 // kv_heads reaches the wave target; otherwise at most target_waves /
@@ -111,6 +129,12 @@ inline unsigned decode_workgroups(const DecodeParams& p, int wpg) {
   long long chunks = p.target_waves / p.kv_heads;
   if (chunks < 1) chunks = 1;
   return (unsigned)((full < chunks ? full : chunks) * groups);
+}
+
+// Extra workgroups of an append-mode launch: one wave per (sequence, kv head).
+inline unsigned append_workgroups(const DecodeParams& p, int wpg) {
+  if (p.k_new == nullptr) return 0;
+  return (unsigned)(((long long)p.batch * p.kv_heads + wpg - 1) / wpg);
 }
 
 // Launchers return hipSuccess or the launch error.  `kv` is the cache

@@ -44,7 +44,7 @@ namespace pa {
 
 struct Segment {
   int b;      // sequence, or -1: no item for this workgroup
-  int len;    // context_lens[b] - token_offset when already read, else -1
+  int len;    // seq_len(p, b) when already read, else -1
   int j0;     // first block of the segment within the sequence's table row
   int nblk;   // blocks of the segment (the kernel clamps by the length)
   int rec;    // record index within the (sequence, head) row
@@ -123,7 +123,7 @@ __device__ inline Segment locate_work(const DecodeParams& p, int groups) {
     return s;
   }
   const int lane = threadIdx.x & 63;
-  auto length = [&](int b) { return b < p.batch ? p.context_lens[b] - p.token_offset : 0; };
+  auto length = [&](int b) { return b < p.batch ? seq_len(p, b) : 0; };
   const int len0 = length(lane);             // batches of up to 64 need one load
   const int nb0 = blocks_of(p, len0);
   auto nb_of = [&](int b0) { return b0 == 0 ? nb0 : blocks_of(p, length(b0 + lane)); };
@@ -168,7 +168,7 @@ __device__ inline bool next_segment(const DecodeParams& p, Segment& s) {
   int b = s.b, L = 0, nb = 0;
   while (nb == 0 && b + 1 < p.batch) {
     ++b;
-    L = p.context_lens[b] - p.token_offset;
+    L = seq_len(p, b);
     nb = blocks_of(p, L);
   }
   if (nb == 0) return false;                 // not reached: F < end <= T

@@ -9,16 +9,10 @@
 // PhysicalPagePool.write_page (storage[page, kv, layer, offset] = data), and
 // WriteKV in section "踩坑三" of the zskr.cn ATB PagedAttention article.
 //
-// The int8 write quantises each (token, kv head) row of head_dim values on
-// the way in, following KVCacheQuantizer.quantize's per_channel branch in the
-// same discosf.com section: scale = absmax / 127 in fp32 (zero -> 1.0),
-// code = clip(round-half-even(x / scale), -128, 127), fp32 IEEE division.
-//
-// The FP8 write (OCP E4M3, the other 8-bit precision "二、优化方向" of the
-// discosf.com article names) applies the same per-row rule with E4M3's
-// largest finite value: scale = absmax / 448, code = the E4M3 value nearest
-// to x / scale, ties to the even code, saturating at +-448.
+// The int8 and FP8 writes quantise each (token, kv head) row of head_dim
+// values on the way in (per-row scale, quant.h).
 #include "pa_internal.h"
+#include "quant.h"
 
 namespace pa {
 namespace {
@@ -41,36 +35,6 @@ __global__ __launch_bounds__(kThreads) void write_kv_f16_kernel(const WriteParam
   }
 }
 
-// Nearest OCP E4M3 code to a finite fp32 value: ties to the even code,
-// magnitudes at or above 448 saturate to 448 (0x7E); the sign bit is y's.
-__device__ __forceinline__ uint8_t e4m3_code(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(y);
-  uint32_t mag;
-  if (!(a < 448.0f)) {
-    mag = 0x7E;
-  } else if (a < 0.015625f) {
-    // below the smallest normal 2^-6 the codes are the multiples of 2^-9
-    // (8 * 2^-9 is the smallest normal, code 0x08)
-    mag = (uint32_t)rintf(a * 512.0f);
-  } else {
-    const uint32_t au = u & 0x7FFFFFFFu;
-    uint32_t e = (au >> 23) - 127u + 7u;     // biased E4M3 exponent, 1 .. 15
-    uint32_t m = (au >> 20) & 7u;            // top three mantissa bits
-    const uint32_t rest = au & 0xFFFFFu;     // the 20 bits dropped
-    if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) {
-      if (++m == 8u) {
-        m = 0;
-        ++e;
-      }
-    }
-    mag = (e << 3) | m;
-    if (mag > 0x7Eu) mag = 0x7E;
-  }
-  return (uint8_t)(sign | mag);
-}
-
 // One wave per (token, kv head) row; lane holds D/64 consecutive elements.
 // FP8 = false: int8 codes; true: E4M3 codes.
 template <int D, bool FP8>
@@ -83,23 +47,10 @@ __device__ __forceinline__ void quantise_row(const uint16_t* src, uint8_t* dst, 
     _Float16 h = __builtin_bit_cast(_Float16, src[lane * PER + e]);
     x[e] = (float)h;
   }
-  float amax = 0.f;
+  uint8_t code[PER];
+  const float s = quantise_vals<PER, FP8>(x, code);
 #pragma unroll
-  for (int e = 0; e < PER; ++e) amax = fmaxf(amax, fabsf(x[e]));
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  float s = __fdiv_rn(amax, FP8 ? 448.0f : 127.0f);
-  s = (s > 0.f) ? s : 1.0f;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const float y = __fdiv_rn(x[e], s);
-    if constexpr (FP8) {
-      dst[lane * PER + e] = e4m3_code(y);
-    } else {
-      const float qv = fminf(fmaxf(rintf(y), -128.f), 127.f);
-      dst[lane * PER + e] = (uint8_t)(int8_t)(int)qv;
-    }
-  }
+  for (int e = 0; e < PER; ++e) dst[lane * PER + e] = code[e];
   if (lane == 0) *scale_dst = s;
 }
 
