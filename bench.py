@@ -76,16 +76,15 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("decode.hip", "decode_mfma.hip", "merge.hip", "work_split.h", "pa_internal.h",
-                  "pa_api.hip", "write_kv.hip")
-
-
 def source_hash() -> str:
-    """Hash of the kernel sources; counter summaries carry the hash they were
-    taken on and are ignored once it changes."""
+    """Hash of the library sources (every file under csrc/); counter
+    summaries carry the hash they were taken on and are ignored once it
+    changes."""
+    csrc = os.path.join(ROOT, "paged_kv_cache_238_amd", "csrc")
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_kv_cache_238_amd", "csrc", name), "rb") as f:
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 

@@ -16,8 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.hip", "decode.hip", "decode_mfma.hip", "merge.hip", "write_kv.hip",
-           "copy_blocks.hip"]
+SOURCES = ["pa_api.hip", "decode.hip", "decode_mfma.hip", "decode_prefix.hip", "merge.hip",
+           "write_kv.hip", "copy_blocks.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -201,14 +201,19 @@ int prefix_partition(int batch, int q_heads, int kv_heads, int prefix_len) {
   return (int)P;
 }
 
-// Partition of the private suffixes: at most eight per suffix, at least one
-// block, at most kRunPartition.  Suffixes are short and uneven (up to a few
-// hundred tokens on top of a long shared prefix), so finer partitions even
-// out the waves: on 64 suffixes of 16..512 tokens at 32 kv heads, 64-token
-// partitions beat 128, 256 and 512 (shared-prefix call 73.6 vs 76.2 us at 256).
+// Partition of the private suffixes: the longest suffix split into at most
+// PA_SUFFIX_SPLIT partitions, at least one block, at most kRunPartition.
+// Suffixes are short and uneven (up to a few hundred tokens on top of a long
+// shared prefix), so finer partitions even out the waves.  On 64 suffixes
+// of 16..512 tokens at 32 kv heads, with the prefix work in the same launch,
+// 128-token partitions (4) took the call to 67.8-68.1 us, against 68.9-69.2
+// at 64 (8), 71.1-71.6 at 256 and 512, and 76.1-76.5 at 32 (16).
+#ifndef PA_SUFFIX_SPLIT
+#define PA_SUFFIX_SPLIT 4
+#endif
 int suffix_partition(int suffix_max) {
   const int blocks = (suffix_max + kBlockTokens - 1) / kBlockTokens;
-  const int P = (blocks + 7) / 8 * kBlockTokens;
+  const int P = (blocks + PA_SUFFIX_SPLIT - 1) / PA_SUFFIX_SPLIT * kBlockTokens;
   return P < kBlockTokens ? kBlockTokens : P > kRunPartition ? kRunPartition : P;
 }
 
@@ -280,8 +285,6 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   ps.max_context_len = suf_max;
   ps.n_part = n_suf;
   ps.rec_stride = rec.suf.stride;
-  st = status_of(pa::launch_decode(ps, kv, s));
-  if (st != PA_OK) return st;
 
   // Prefix: one record per (sequence, query head, prefix partition).
   pa::DecodeParams pp = p;
@@ -293,7 +296,8 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   pp.n_part = n_pre;
   pp.rec_stride = n_pre;
   pp.prefix_tiles = tiles;
-  st = status_of(pa::launch_prefix_mfma(pp, kv, s));
+  // Both record sets in one launch (decode_prefix.hip), then the merge.
+  st = status_of(pa::launch_shared_prefix(ps, pp, kv, s));
   if (st != PA_OK) return st;
 
   pa::MergeParams mp = {};

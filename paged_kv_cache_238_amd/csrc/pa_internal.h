@@ -143,8 +143,9 @@ inline unsigned append_workgroups(const DecodeParams& p, int wpg) {
 hipError_t launch_decode(const DecodeParams& p, int kv, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int kv, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv, hipStream_t stream);
-// Shared prefix: records of every (sequence, query head) over the prefix.
-hipError_t launch_prefix_mfma(const DecodeParams& p, int kv, hipStream_t stream);
+// Suffix partition work and prefix work of the shared-prefix call in one launch.
+hipError_t launch_shared_prefix(const DecodeParams& ps, const DecodeParams& pp, int kv,
+                                hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_write_kv(const WriteParams& p, hipStream_t stream);
 hipError_t launch_write_kv_int8(const WriteParams& p, hipStream_t stream);

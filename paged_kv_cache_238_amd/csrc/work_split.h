@@ -102,11 +102,11 @@ __device__ inline int blocks_of(const DecodeParams& p, int L) {
   return (L > 0 && L <= p.max_context_len) ? (L + kBlockTokens - 1) / kBlockTokens : 0;
 }
 
-// First segment of this workgroup.  Must be called by all 64 lanes of each
-// wave; the result is wave-uniform.
-__device__ inline Segment locate_work(const DecodeParams& p, int groups) {
-  Segment s{-1, -1, 0, 0, 0, (int)(blockIdx.x % groups), 0, 0, -1, 0};
-  const int item = blockIdx.x / groups;      // head groups fastest
+// First segment of workgroup `wg` of the launch's partition work.  Must be
+// called by all 64 lanes of each wave; the result is wave-uniform.
+__device__ inline Segment locate_work(const DecodeParams& p, int groups, int wg) {
+  Segment s{-1, -1, 0, 0, 0, wg % groups, 0, 0, -1, 0};
+  const int item = wg / groups;              // head groups fastest
   const int P = p.partition_size;
   if (p.direct) {                            // empty or invalid sequences included
     if (item < p.batch) {

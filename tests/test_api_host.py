@@ -150,19 +150,19 @@ def _sp_bytes(B, Hq, D, n_suf, n_pre):
 
 
 def test_shared_prefix_workspace_size():
-    # suffix records: a 512-token suffix is 32 blocks, at most eight
-    # partitions of 4 blocks (64 tokens), so 8 of them; prefix records: 4
-    # query tiles x 32 kv heads = 128 waves per prefix partition, so
-    # 128-token partitions (about 1024 waves), 8 of them
+    # suffix records: a 512-token suffix is 32 blocks, at most four
+    # partitions of 8 blocks (128 tokens), so 4 of them (+1 per row); prefix
+    # records: 4 query tiles x 32 kv heads = 128 waves per prefix partition,
+    # so 128-token partitions (about 1024 waves), 8 of them
     rows = 64 * 32
-    suf = 512 + rows * 9 * 8 + rows * 9 * 256
+    suf = 512 + rows * 5 * 8 + rows * 5 * 256
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
         suf + rows * 8 * 8 + rows * 8 * 256
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
-        _sp_bytes(64, 32, 128, 8, 8)
+        _sp_bytes(64, 32, 128, 4, 8)
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1000) == 0
     # longer suffixes: 4096 - 1024 = 3072 tokens, 192 blocks; partitions of
-    # 24 blocks would exceed 256 tokens, so 256 (12 partitions); prefix: one
+    # 48 blocks would exceed 256 tokens, so 256 (12 partitions); prefix: one
     # query tile x 8 kv heads = 8 waves per partition, so one-block
     # partitions, 64 of them
     assert pa.shared_prefix_workspace_size(8, 8, 8, 128, 4096, 1024) == \
