@@ -395,11 +395,13 @@ int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,
  *   workspace        pa_decode_shared_prefix_workspace_size(...) bytes,
  *                    required (the split always runs).
  *   all other arguments as for pa_decode / pa_decode_int8 / pa_decode_fp8;
- *   the suffixes use the library's 256-token partitions.
+ *   the suffixes are split into at most four partitions of 16 to 256
+ *   tokens (by the longest suffix, max_context_len - prefix_len).
  *
  * Returns PA_ERR_SHAPE for a bad prefix_len, otherwise the codes of
- * pa_decode.  Launches, in order on `stream`: the suffix partition kernel,
- * the prefix kernel and the merge kernel.
+ * pa_decode.  Launches, in order on `stream`: one kernel holding both the
+ * prefix work and the suffix partition work (independent record sets), then
+ * the merge kernel.
  */
 size_t pa_decode_shared_prefix_workspace_size(int batch, int q_heads, int kv_heads,
                                               int head_dim, int max_context_len,
