@@ -11,7 +11,7 @@ using namespace valu;
 // index (the shared-prefix launch runs it on part of its grid).
 template <int D, int G, int KV>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParams p) {
-  valu_body<D, G, KV>(p, (int)blockIdx.x);
+  valu_body<D, G, KV, true>(p, (int)blockIdx.x);
 }
 
 // Waves (kv heads) per workgroup: four when the heads divide evenly.

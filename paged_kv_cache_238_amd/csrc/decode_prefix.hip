@@ -30,7 +30,7 @@ void shared_prefix_kernel(const DecodeParams ps, const DecodeParams pp, int pref
   if (wg < prefix_groups) {
     mfma::mfma_body<D, 16, KV, true>(pp, wg);
   } else if constexpr (G <= 2) {
-    valu::valu_body<D, G, KV>(ps, wg - prefix_groups);
+    valu::valu_body<D, G, KV, false>(ps, wg - prefix_groups);
   } else {
     mfma::mfma_body<D, G, KV, false>(ps, wg - prefix_groups);
   }
