@@ -66,6 +66,12 @@ constexpr int kRowPad = PA_V_ROW_PAD;   // bytes of padding per LDS row of the V
 #ifndef PA_MFMA_WAVES_PER_EU
 #define PA_MFMA_WAVES_PER_EU 3
 #endif
+#ifndef PA_MFMA_WHOLE_LINE
+#define PA_MFMA_WHOLE_LINE 1
+#endif
+#ifndef PA_MFMA_KV_NT
+#define PA_MFMA_KV_NT 1
+#endif
 // The running max is only moved (and the accumulators rescaled) when a block
 // beats it by more than this many log2 units; softmax is invariant to the
 // reference point, and probabilities stay <= 2^8, well inside fp16.
@@ -107,6 +113,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// K/V loads; NT: the non-temporal cache policy (whole lines read once).
+template <bool NT>
+__device__ __forceinline__ uint4 buffer_load16_kv(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  u32x4 v = NT ? __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2)
+               : __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Lane l ^ 8 within each row of 16 lanes (DPP row rotation by 8).
+__device__ __forceinline__ uint32_t swap8(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
 }
 
 // Four int8 codes -> four exact fp16 values.
@@ -156,12 +175,12 @@ __device__ __forceinline__ void f8x16_to_h16(const uint4& c, uint4& first, uint4
 }
 
 // Which bytes of a block each lane loads, and which head-dim elements it then
-// feeds to the QK product: load ld has lane (li, g) read bytes 64 ld + 16 g
-// .. + 15 of its head's row in token li, so each load covers 64 bytes of all
-// 16 rows and lane (li, g) holds row li, as the A operand wants.  (Loads of
-// whole 128-byte lines, 8 rows per instruction, with a DPP exchange between
-// lanes l and l ^ 8 to restore the operand layout, measured 1-2 % slower:
-// the exchange costs more than the wider lines save.)
+// feeds to the QK product: in the operand layout lane (li, g) holds bytes
+// 64 ld + 16 g .. + 15 of its head's row in token li, as the A operand
+// wants.  The loads themselves read whole 128-byte lines (see load_row), so
+// each line is consumed by one instruction and can carry the non-temporal
+// cache policy; with the default policy the half-line layout and the
+// whole-line one measured within 2 %.
 template <int D, bool I8>
 struct Geometry {
   static constexpr int kEsz = I8 ? 1 : 2;
@@ -174,10 +193,32 @@ struct Geometry {
     if constexpr (I8) return 64 * (kk / 2) + 16 * g + 8 * (kk % 2) + j;
     else return 32 * kk + 8 * g + j;
   }
-  // Token row (0..15) and byte offset within the head's row of load ld.
-  static __device__ __forceinline__ int load_row(int ld, int lane) { return lane & 15; }
+  // Loads come in pairs over one 128-byte line of every token row
+  // (whole-line mode, when a head's row spans at least one line): load 2m
+  // reads rows 0..7 and load 2m+1 rows 8..15, each row's whole line, so no
+  // line is left half read.  Lane (li, lg) of load 2m reads row li & 7 at
+  // chunk lg (li < 8) or lg + 4 (li >= 8); of load 2m+1, row 8 + (li & 7) at
+  // chunk lg (li >= 8) or lg + 4 (li < 8) (16-byte chunks of the line).  So
+  // lane (li, lg) already holds chunk lg of its own row li in one of the
+  // two, and chunk lg + 4 of row li sits in lane (li ^ 8, lg) of the other:
+  // one select and one DPP row rotation by 8 restore the operand layout
+  // below (kswap).  Otherwise (a 64-byte row) load ld reads bytes
+  // 64 ld + 16 lg of row li.
+  static constexpr bool kWholeLine = kLoads >= 2 && PA_MFMA_WHOLE_LINE;
+  static __device__ __forceinline__ int load_row(int ld, int lane) {
+    const int li = lane & 15;
+    if constexpr (kWholeLine) return (ld & 1) ? 8 + (li & 7) : (li & 7);
+    else return li;
+  }
   static __device__ __forceinline__ int load_col(int ld, int lane) {
-    return 64 * ld + 16 * (lane >> 4);
+    const int li = lane & 15, lg = lane >> 4;
+    if constexpr (kWholeLine) {
+      const bool low = li < 8;
+      const int chunk = lg + (((ld & 1) ? low : !low) ? 4 : 0);
+      return 128 * (ld >> 1) + 16 * chunk;
+    } else {
+      return 64 * ld + 16 * lg;
+    }
   }
   static constexpr int kRowBytes = D * 2 + kRowPad;   // LDS row of the fp16 V tile
 };
@@ -210,6 +251,7 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
   using Geo = Geometry<D, I8>;
   constexpr int NLD = Geo::kLoads;
   constexpr int NKK = Geo::kSteps;
+  constexpr bool kLineNT = Geo::kWholeLine && PA_MFMA_KV_NT;
   constexpr int NT = D / 16;                 // O^T tiles of 16 dims
   constexpr int ESZ = I8 ? 1 : 2;
   constexpr int TILE = kBlockTokens * Geo::kRowBytes;
@@ -399,9 +441,9 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)blk * blk_bytes, nbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)blk * blk_bytes, nbytes);
 #pragma unroll
-    for (int ld = 0; ld < NLD; ++ld) R.k[ld] = buffer_load16(rk, ld_off[ld]);
+    for (int ld = 0; ld < NLD; ++ld) R.k[ld] = buffer_load16_kv<kLineNT>(rk, ld_off[ld]);
 #pragma unroll
-    for (int ld = 0; ld < NLD; ++ld) R.v[ld] = buffer_load16(rv, ld_off[ld]);
+    for (int ld = 0; ld < NLD; ++ld) R.v[ld] = buffer_load16_kv<kLineNT>(rv, ld_off[ld]);
     if constexpr (I8) {
       // scales [NB, Hkv, 16] of kv head g: one float per lane, rotated by
       // 4 lg within each row of 16 lanes so that the four tokens 4 lg .. 4 lg+3
@@ -420,19 +462,34 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
   auto process_block = [&](auto tail_tag, const Regs& R, int valid) {
     constexpr bool TAIL = decltype(tail_tag)::value;
     // K as fp16 A operands, one per QK step.
+    // K in the operand layout: lane (li, lg) holds bytes 64 ld + 16 lg of
+    // row li in kr[ld] (whole-line loads: a select and a swap, see Geometry).
+    uint4 kr[NLD];
+#pragma unroll
+    for (int m = 0; m < NLD; m += (Geo::kWholeLine ? 2 : 1)) {
+      if constexpr (Geo::kWholeLine) {
+        const bool low = li < 8;
+        const uint4 x = R.k[m], y = R.k[m + 1];
+        const uint4 own = low ? x : y, other = low ? y : x;
+        kr[m] = own;
+        kr[m + 1] = make_uint4(swap8(other.x), swap8(other.y), swap8(other.z), swap8(other.w));
+      } else {
+        kr[m] = R.k[m];
+      }
+    }
     h8 kA[NKK];
     if constexpr (I8) {
 #pragma unroll
       for (int ld = 0; ld < NLD; ++ld) {
         uint4 a, c;
-        if constexpr (KV == kKvI8) i8x16_to_h16_biased(R.k[ld], a, c);
-        else f8x16_to_h16(R.k[ld], a, c);
+        if constexpr (KV == kKvI8) i8x16_to_h16_biased(kr[ld], a, c);
+        else f8x16_to_h16(kr[ld], a, c);
         kA[2 * ld] = __builtin_bit_cast(h8, a);
         kA[2 * ld + 1] = __builtin_bit_cast(h8, c);
       }
     } else {
 #pragma unroll
-      for (int ld = 0; ld < NLD; ++ld) kA[ld] = __builtin_bit_cast(h8, R.k[ld]);
+      for (int ld = 0; ld < NLD; ++ld) kA[ld] = __builtin_bit_cast(h8, kr[ld]);
     }
     f4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
