@@ -20,7 +20,9 @@ kernels).  "cold" repeats steps one at a time with L2 and MALL flushed first.
 "roofline" describes the dominant kernel (the decode partition kernel):
 achieved = its algorithmic bytes (the KV bytes it must read) / its mean
 duration, timed with HIP events recorded on the stream it runs on, around
-each launch inside the timed steps.  "traffic" comes from rocprofv3 counter
+the launch of every fifth timed step (--event-every; an event is a marker in
+the stream and costs the step a few microseconds, so the other steps run
+without).  "traffic" comes from rocprofv3 counter
 summaries committed under profiles/ and is null unless they were taken on
 the current kernel source.  "cpu_baseline" times the fp64 CPU oracle on a
 bounded sample of the same workload.
@@ -61,6 +63,9 @@ def parse():
     ap.add_argument("--shared-prefix", action="store_true",
                     help="run the workload through the shared-prefix entry point "
                          "(workloads with a shared prefix only)")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="bracket the decode kernel of every N-th timed step with HIP events "
+                         "(the kernel mean comes from those launches)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed one by one with L2 and MALL flushed before "
                          "each (reported under 'cold'; 0 to skip)")
@@ -164,21 +169,30 @@ class Case:
             self.pa.merge_partials(self.ws, self.cl, wl.q_heads, wl.head_dim, self.P,
                                    wl.max_context_len, out=self.out)
 
-    def run(self, steps, warmup):
+    def run(self, steps, warmup, event_every=1):
+        """Warm-up, then `steps` timed steps.  The decode kernel of every
+        `event_every`-th timed step is bracketed by HIP events on its stream
+        (each event is a marker in the stream, and the steps between two
+        sampled ones run without them)."""
         torch = self.torch
         for _ in range(warmup):
             self.write()
             self.decode_kernel()
             self.merge()
+        every = max(1, int(event_every))
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
+              for _ in range(0, steps, every)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for a, b in ev:
+        for i in range(steps):
             self.write()
-            a.record()
-            self.decode_kernel()
-            b.record()
+            if i % every == 0:
+                a, b = ev[i // every]
+                a.record()
+                self.decode_kernel()
+                b.record()
+            else:
+                self.decode_kernel()
             self.merge()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -386,7 +400,7 @@ def main():
     if args.shared_prefix and not pre:
         raise SystemExit(f"--shared-prefix: workload {args.workload} has no shared prefix")
     head = Case(pa, torch, gen, args.workload, args.partition_size, dev, shared_prefix=pre)
-    wall, kern = head.run(args.steps, args.warmup)
+    wall, kern = head.run(args.steps, args.warmup, args.event_every)
     s = summarize(head, wall, kern, args.steps)
     s["cold"] = cold_summary(head, args.cold_steps)
     print(f"[bench] {args.workload}: {s['ms_per_step']} ms/step, decode kernel "
@@ -399,7 +413,7 @@ def main():
     others = []
     for name in [n for n in args.others.split(",") if n and n != args.workload]:
         c = Case(pa, torch, gen, name, -1, dev)
-        w2, k2 = c.run(max(20, args.steps // 2), max(5, args.warmup // 2))
+        w2, k2 = c.run(max(20, args.steps // 2), max(5, args.warmup // 2), args.event_every)
         o = summarize(c, w2, k2, max(20, args.steps // 2))
         o["cold"] = cold_summary(c, args.cold_steps)
         others.append(o)
@@ -411,7 +425,7 @@ def main():
         if name == "prefix_shared":
             # the same workload through the shared-prefix entry point
             c = Case(pa, torch, gen, name, -1, dev, shared_prefix=gen.SPECS[name]["prefix"])
-            w2, k2 = c.run(max(20, args.steps // 2), max(5, args.warmup // 2))
+            w2, k2 = c.run(max(20, args.steps // 2), max(5, args.warmup // 2), args.event_every)
             o = summarize(c, w2, k2, max(20, args.steps // 2))
             o["cold"] = cold_summary(c, args.cold_steps)
             others.append(o)
@@ -446,6 +460,7 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes_per_launch": s["kv_bytes"],
                      "launch_us_mean": s["decode_kernel_us_mean"],
+                     "launches_timed": len(kern),
                      "traffic": traffic_for(args.workload),
                      "source_hash": source_hash()},
         "cold": s["cold"],
