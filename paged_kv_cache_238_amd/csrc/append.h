@@ -49,8 +49,8 @@ __device__ __forceinline__ void append_token(const DecodeParams& p, int pair) {
     if (!bad) {
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        static_cast<uint16_t*>(const_cast<void*>(p.k_pool))[dst + e] = p.k_new[src + e];
-        static_cast<uint16_t*>(const_cast<void*>(p.v_pool))[dst + e] = p.v_new[src + e];
+        static_cast<uint16_t*>(p.k_pool_w)[dst + e] = p.k_new[src + e];
+        static_cast<uint16_t*>(p.v_pool_w)[dst + e] = p.v_new[src + e];
       }
     }
   } else {
@@ -66,8 +66,8 @@ __device__ __forceinline__ void append_token(const DecodeParams& p, int pair) {
     if (!bad) {
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        static_cast<uint8_t*>(const_cast<void*>(p.k_pool))[dst + e] = kc[e];
-        static_cast<uint8_t*>(const_cast<void*>(p.v_pool))[dst + e] = vc[e];
+        static_cast<uint8_t*>(p.k_pool_w)[dst + e] = kc[e];
+        static_cast<uint8_t*>(p.v_pool_w)[dst + e] = vc[e];
       }
       if (lane == 0) {
         const size_t sidx = ((size_t)blk * Hkv + g) * kBlockTokens + t % kBlockTokens;

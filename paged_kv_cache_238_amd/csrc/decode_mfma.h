@@ -110,11 +110,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 // K/V loads; NT: the non-temporal cache policy (whole lines read once).
 template <bool NT>
 __device__ __forceinline__ uint4 buffer_load16_kv(__amdgpu_buffer_rsrc_t r, uint32_t off) {

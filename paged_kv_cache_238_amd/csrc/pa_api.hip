@@ -369,6 +369,8 @@ int append_common(void* out, float* lse_out, const void* q, const void* k_new, c
   p.v_pool = v_pool;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  p.k_pool_w = k_pool;
+  p.v_pool_w = v_pool;
   p.k_scale_w = k_scale;
   p.v_scale_w = v_scale;
   p.k_new = static_cast<const uint16_t*>(k_new);

@@ -59,7 +59,9 @@ struct DecodeParams {
   int main_groups;            // workgroups of the partition work (append mode)
   const uint16_t* k_new;      // fp16 [B, Hkv, D]
   const uint16_t* v_new;
-  float* k_scale_w;           // 8-bit pools: the scales the append writes
+  void* k_pool_w;             // the pools and (8-bit) scales the append writes
+  void* v_pool_w;
+  float* k_scale_w;
   float* v_scale_w;
   float2* app_ml;
   uint16_t* app_o;
