@@ -202,7 +202,10 @@ size_t pa_decode_workspace_size(int batch, int q_heads, int kv_heads, int head_d
  *                    (may be NULL when that is 0); not shared by
  *                    concurrent calls
  * L_b = 0 gives a zero output row and lse = -inf.  fp32 accumulation,
- * output rounded to fp16 to nearest even.
+ * output rounded to fp16 to nearest even.  K/V are loaded with the
+ * non-temporal cache policy (each block is read once per call); tables that
+ * alias blocks across sequences (a shared prefix) are served faster by
+ * pa_decode_shared_prefix.
  */
 int pa_decode(void* out, float* lse_out, const void* q, const void* k_pool,
               const void* v_pool, const int32_t* block_table, int max_blocks,
