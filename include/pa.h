@@ -399,7 +399,8 @@ int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,
  *                    required (the split always runs).
  *   all other arguments as for pa_decode / pa_decode_int8 / pa_decode_fp8;
  *   the suffixes are split into at most four partitions of 16 to 256
- *   tokens (by the longest suffix, max_context_len - prefix_len).
+ *   tokens (by the longest suffix, max_context_len - prefix_len), and the
+ *   suffix work is cut into balanced chunks of at most one partition.
  *
  * Returns PA_ERR_SHAPE for a bad prefix_len, otherwise the codes of
  * pa_decode.  Launches, in order on `stream`: one kernel holding both the

@@ -207,7 +207,8 @@ int prefix_partition(int batch, int q_heads, int kv_heads, int prefix_len) {
 // shared prefix), so finer partitions even out the waves.  On 64 suffixes
 // of 16..512 tokens at 32 kv heads, with the prefix work in the same launch,
 // 128-token partitions (4) took the call to 67.8-68.1 us, against 68.9-69.2
-// at 64 (8), 71.1-71.6 at 256 and 512, and 76.1-76.5 at 32 (16).
+// at 64 (8), 71.1-71.6 at 256 and 512, and 76.1-76.5 at 32 (16) (partition
+// items; with the balanced chunks 4 and 8 measured alike, 2 slower).
 #ifndef PA_SUFFIX_SPLIT
 #define PA_SUFFIX_SPLIT 4
 #endif
@@ -285,6 +286,14 @@ int prefix_common(void* out, float* lse_out, const void* q, const void* k_pool,
   ps.max_context_len = suf_max;
   ps.n_part = n_suf;
   ps.rec_stride = rec.suf.stride;
+  // Balanced chunks over the suffixes even when the (sequence, kv head)
+  // pairs alone reach the wave target: a wave target of one wave per
+  // partition item caps the chunks at one partition, so the uneven suffixes
+  // are cut into equal pieces instead of partitions that end early.  On 64
+  // suffixes of 16..512 tokens at 32 kv heads the call took 66.1 against
+  // 68.0 us with partition items (three alternating runs on one box).
+  const long long suffix_items = (long long)n_suf * batch * kv_heads;
+  if (suffix_items > ps.target_waves) ps.target_waves = (int)suffix_items;
 
   // Prefix: one record per (sequence, query head, prefix partition).
   pa::DecodeParams pp = p;
