@@ -139,3 +139,24 @@ def test_full_size_prefix_workload_sampled_rows(pa):
     want, _ = oracle_decode(wl, host, rows=rows)
     got = np.stack([out[b, h] for b, h in rows])
     check_close(got, np.stack([want[b, h] for b, h in rows]), "prefix_shared sampled rows")
+
+
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
+def test_many_pairs_balanced_suffix_chunks(pa, kv):
+    """(sequence, kv head) pairs past 2048 with suffixes split into several
+    partitions: the suffix work runs as balanced chunks of at most one
+    partition; every row against the oracle, empty suffixes included."""
+    over = dict(batch=130, q_heads=32, kv_heads=16, head_dim=64, prefix=32, smin=1, smax=200,
+                kv_dtype=kv)
+    wl = gen.make("prefix_shared", seed=70 + len(kv), small=True, overrides=over)
+    pre = prefix_len_of(wl)
+    assert pre == 32 and wl.batch * wl.kv_heads >= 2048
+    wl.context_lens[[3, 77]] = pre           # exactly the prefix: empty suffix
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    d = device_inputs(wl, vals)
+    d["context_lens"] = t(wl.context_lens)
+    say(f"many pairs kv={kv} B={wl.batch} max_ctx={wl.max_context_len}")
+    out, lse = run_prefix(pa, wl, d, pre)
+    want, want_lse = oracle_decode(wl, vals)
+    check_close(out.cpu().numpy(), want, f"many pairs kv={kv}")
+    np.testing.assert_allclose(lse.cpu().numpy(), want_lse, rtol=0, atol=1e-4)
