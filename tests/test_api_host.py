@@ -49,7 +49,7 @@ def dec(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), NULL), (dict(out=None), NULL), (dict(bt=None), NULL), (dict(cl=None), NULL),
     (dict(Hq=6, Hkv=4), SHAPE), (dict(Hkv=0), SHAPE), (dict(B=-1), SHAPE), (dict(NB=0), SHAPE),
-    (dict(mcl=257), SHAPE), (dict(mcl=-1), SHAPE), (dict(B=70000), SHAPE),
+    (dict(mcl=257), SHAPE), (dict(mcl=-1), SHAPE), (dict(B=70000), SHAPE), (dict(B=65536), SHAPE),
     (dict(bs=32), UNSUP), (dict(D=96), UNSUP), (dict(Hq=24, Hkv=1), UNSUP),
     (dict(Hq=64, Hkv=2), UNSUP), (dict(P=24), UNSUP), (dict(P=-16), UNSUP),
     (dict(mcl=256, P=16, ws=None), NULL), (dict(mcl=256, P=16, wsb=100), WS),

@@ -641,3 +641,29 @@ def test_randomized_shapes(pa, i):
     assert not out[~live].any() and np.all(np.isneginf(lse[~live]))
     check_close(out[live], want[live], f"random {i}")
     np.testing.assert_allclose(lse[live], want_lse[live], rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("G,kv", [(2, "fp16"), (4, "int8")])
+@pytest.mark.parametrize("P", [0, 16])
+def test_maximum_batch(pa, G, kv, P):
+    """The largest batch the library accepts (65535 sequences, the merge
+    grid's limit) with short ragged contexts: one partition per sequence
+    (direct) and a forced 16-token split (partition items, then the merge);
+    sampled rows against the oracle, every row finite."""
+    over = dict(batch=65535, q_heads=G, kv_heads=1, head_dim=64, lmin=1, lmax=40,
+                occupancy=0.9, kv_dtype=kv)
+    wl = gen.make("gqa70b_mixed", seed=1900 + G, overrides=over)
+    vals = gen.fill_numpy(wl, new_slot_poison=False)
+    say(f"max batch G={G} kv={kv} P={P} NB={wl.num_blocks}")
+    d = device_inputs(wl, vals)
+    out, lse = gpu_decode(pa, wl, d, partition_size=P)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    rng = np.random.default_rng(wl.seed + P)
+    rows = [(int(rng.integers(wl.batch)), int(rng.integers(wl.q_heads))) for _ in range(60)]
+    rows += [(0, 0), (wl.batch - 1, wl.q_heads - 1)]
+    want, want_lse = oracle_decode(wl, vals, rows=rows)
+    check_close(np.stack([out[b, h] for b, h in rows]),
+                np.stack([want[b, h] for b, h in rows]), f"max batch G={G} kv={kv} P={P}")
+    np.testing.assert_allclose([lse[b, h] for b, h in rows], [want_lse[b, h] for b, h in rows],
+                               rtol=0, atol=1e-4)
