@@ -304,7 +304,8 @@ def counters_summary(args):
     from workloads import gen
     out_json, dfetch, dwrite, cfetch, cwrite = args.counters_summary
     wl = gen.make(args.workload, poison=False)
-    kname = decode_kernel_name(wl)
+    # the shared-prefix entry point's partition work runs in its own kernel
+    kname = "shared_prefix_kernel" if args.shared_prefix else decode_kernel_name(wl)
     known = args.copy_calibration << 20
 
     def pick(table, key):
@@ -324,7 +325,8 @@ def counters_summary(args):
     f_write = known / (cw * 1024.0)
     traffic = df * 1024.0 * f_fetch + dw * 1024.0 * f_write
     res = {
-        "workload": wl.name, "kernel": df_name, "source_hash": source_hash(),
+        "workload": wl.name + (" (shared-prefix path)" if args.shared_prefix else ""),
+        "kernel": df_name, "source_hash": source_hash(),
         "decode_fetch_kib_per_dispatch": df, "decode_write_kib_per_dispatch": dw,
         "decode_dispatches": [df_n, dw_n],
         "copy_kernel": cf_name, "copy_bytes": known,
