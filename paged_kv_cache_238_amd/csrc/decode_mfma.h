@@ -21,6 +21,10 @@
 // is applied to the score and the V scale to the probability.  FP8 (OCP
 // E4M3) caches: every E4M3 value is exact in fp16, two codes per
 // v_cvt_scalef32_pk_f16_fp8 (scale 1); the scales are applied as for int8.
+// The probability times the V scale enters the PV product in fp16, relative
+// to a power of two 2^vexp kept per segment (see vexp below), so small
+// scales do not push it into fp16's subnormal range; finalize multiplies
+// the result back by 2^vexp, exactly.
 //
 // Method and readings are those of the VALU kernel (zskr.cn ATB
 // PagedAttention article, section "PagedAttention 的 Attention 计算修改",
@@ -72,10 +76,22 @@ constexpr int kRowPad = PA_V_ROW_PAD;   // bytes of padding per LDS row of the V
 #ifndef PA_MFMA_KV_NT
 #define PA_MFMA_KV_NT 1
 #endif
+#ifndef PA_MFMA_K_EXACT
+#define PA_MFMA_K_EXACT 0
+#endif
 // The running max is only moved (and the accumulators rescaled) when a block
 // beats it by more than this many log2 units; softmax is invariant to the
 // reference point, and probabilities stay <= 2^8, well inside fp16.
 constexpr float kRescaleSlack = 8.0f;
+// 8-bit caches: the V scales of a block enter the fp16 probabilities as
+// scale * 2^-vexp.  vexp follows the largest scale exponent e of the blocks
+// (floor(log2)), moving only when a block leaves [vexp - kVexpDown,
+// vexp + kVexpUp]; a move multiplies the accumulators by a power of two,
+// exactly.  With p <= 2^8 the fp16 operand stays below 2^(8 + kVexpUp + 1)
+// = 2^15 (finite); a token whose scale is within 2^-kVexpDown of vexp and
+// whose probability is at least 2^-6 stays in fp16's normal range.
+constexpr int kVexpUp = 6;
+constexpr int kVexpDown = 8;
 constexpr int kLongContext = 32768;   // tokens; see waves_per_group
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -400,7 +416,7 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
 
   // int8: sum over head_dim of q for head li (removes the 1152 bias of K).
   float qbias = 0.f;
-  if constexpr (KV == kKvI8) {
+  if constexpr (KV == kKvI8 && !PA_MFMA_K_EXACT) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
@@ -415,6 +431,7 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
   for (int n = 0; n < NT; ++n) acc[n] = f4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf;   // reference max of head li (same in all four lane groups)
   float l_run = 0.f;       // this lane's share of the running sum (its tokens)
+  int vexp = 0;            // 8-bit caches: V-scale exponent reference (wave-uniform)
   bool bad_blk = false;
 
   struct Regs {
@@ -477,7 +494,8 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
 #pragma unroll
       for (int ld = 0; ld < NLD; ++ld) {
         uint4 a, c;
-        if constexpr (KV == kKvI8) i8x16_to_h16_biased(kr[ld], a, c);
+        if constexpr (KV == kKvI8 && PA_MFMA_K_EXACT) i8x16_to_h16(kr[ld], a, c);
+        else if constexpr (KV == kKvI8) i8x16_to_h16_biased(kr[ld], a, c);
         else f8x16_to_h16(kr[ld], a, c);
         kA[2 * ld] = __builtin_bit_cast(h8, a);
         kA[2 * ld + 1] = __builtin_bit_cast(h8, c);
@@ -539,12 +557,40 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - m_use);
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    float sv = 0.f;          // 8-bit: this lane's V scale times 2^-vexp
+    if constexpr (I8) {
+      // The lane holds the scale of token (li + 4 lg) % 16; tail tokens
+      // (whose slots may hold NaN) count as 0.
+      float vs = R.vs;
+      if constexpr (TAIL) {
+        if (((li + 4 * lg) & 15) >= valid) vs = 0.f;
+      }
+      // Largest scale of the block: every row of 16 lanes holds all 16.
+      float vmax = vs;
+      vmax = fmaxf(vmax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(vmax), 0xB1, 0xF, 0xF, false)));
+      vmax = fmaxf(vmax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(vmax), 0x4E, 0xF, 0xF, false)));
+      vmax = fmaxf(vmax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(vmax), 0x141, 0xF, 0xF, false)));
+      vmax = fmaxf(vmax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(vmax), 0x140, 0xF, 0xF, false)));
+      const int ebits = (__builtin_amdgcn_readfirstlane(__float_as_int(vmax)) >> 23) & 0xFF;
+      // Zero (no valid token, or a block outside the pool) and non-finite
+      // scales leave the reference where it is.
+      if (ebits != 0 && ebits != 0xFF) {
+        const int e = ebits - 127;
+        if (e > vexp + kVexpUp || e < vexp - kVexpDown) {
+          const float f = __builtin_ldexpf(1.0f, vexp - e);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[n] *= f;
+          vexp = e;
+        }
+      }
+      sv = __builtin_ldexpf(vs, -vexp);
+    }
     h4 pB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float pv = pr[i];
       if constexpr (I8) {
-        float vsc = scale_of(R.vs, i);
+        float vsc = scale_of(sv, i);
         if constexpr (TAIL) {
           if (4 * lg + i >= valid) vsc = 0.f;
         }
@@ -570,12 +616,15 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
   auto finalize = [&]() {
     float den = l_run;
     den = group_sum(den);
+    // 1 / l, times 2^vexp for 8-bit caches (the V scales entered as
+    // scale * 2^-vexp).
+    const float inv_l = I8 ? __builtin_ldexpf(1.0f / den, vexp) : 1.0f / den;
     if (qrow >= 0) {
       const size_t row = (size_t)qrow;
       float M = m_run;
       if (bad_blk) M = den = __builtin_nanf("");
       if (p.direct) {
-        const float inv = 1.0f / den;
+        const float inv = inv_l;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           uint2 o;
@@ -591,7 +640,7 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
         // o / l in fp16 (a convex combination of V rows, so within V's
         // range); (m, l) stay fp32.
         const size_t rec = row * p.rec_stride + ridx;
-        const float inv = 1.0f / den;
+        const float inv = inv_l;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           uint2 o;

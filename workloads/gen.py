@@ -22,13 +22,19 @@ Recipe (seed = 2380 + config index unless given):
   rng = numpy.random.default_rng(seed); structure first (lengths, tables),
   then values in the order q, k_pool, v_pool, k_new, v_new, each
   rng.standard_normal(dtype=float32).astype(float16).  int8 pools draw codes
-  uniformly from [-127, 127] and scales uniformly from [2.3/127, 3.8/127]
+  uniformly from [-128, 127] and scales uniformly from [2.3/127, 3.8/127]
   (the range of absmax/127 for 128 N(0,1) values).  fp8 pools (OCP E4M3,
   stored as raw uint8 codes) draw codes uniformly from the 254 finite codes
-  (every code but 0x7F and 0xFF) and scales from [2.3/448, 3.8/448].  Poisoned runs fill every
-  block no table references and every tail slot (token >= L in a sequence's
-  last block) with fp16 NaN (int8 / fp8 pools: NaN scales), so a stray read
-  shows.
+  (every code but 0x7F and 0xFF) and scales from [2.3/448, 3.8/448].
+  Poisoned runs fill every block no table references and every tail slot
+  (token >= L in a sequence's last block) with fp16 NaN (int8 / fp8 pools:
+  NaN scales), so a stray read shows.
+  Source mode (fill_source_numpy / fill_source_torch) draws the long-context
+  8-bit workloads as their configuration states them: fp16 N(0,1) K / V for
+  every slot of the pool, in the order q, k_src, v_src, k_new, v_new; the
+  caller quantises them into codes and scales with a quantiser of its own
+  (the library's quantising write, or the oracle's), so this module still
+  holds none of that arithmetic.
   The torch backend draws the same kind of values on the device with a seeded
   torch.Generator (used for full-size workloads; values differ from numpy's).
 """
@@ -280,8 +286,8 @@ def fill_numpy(wl: Workload, *, new_slot_poison: bool = True) -> dict[str, np.nd
         v["k_scale"] = rng.uniform(2.3 / 448, 3.8 / 448, size=(NB, Hkv, BLOCK)).astype(np.float32)
         v["v_scale"] = rng.uniform(2.3 / 448, 3.8 / 448, size=(NB, Hkv, BLOCK)).astype(np.float32)
     else:
-        v["k_pool"] = rng.integers(-127, 128, size=(NB, BLOCK, Hkv, D), dtype=np.int8)
-        v["v_pool"] = rng.integers(-127, 128, size=(NB, BLOCK, Hkv, D), dtype=np.int8)
+        v["k_pool"] = rng.integers(-128, 128, size=(NB, BLOCK, Hkv, D), dtype=np.int8)
+        v["v_pool"] = rng.integers(-128, 128, size=(NB, BLOCK, Hkv, D), dtype=np.int8)
         v["k_scale"] = rng.uniform(2.3 / 127, 3.8 / 127, size=(NB, Hkv, BLOCK)).astype(np.float32)
         v["v_scale"] = rng.uniform(2.3 / 127, 3.8 / 127, size=(NB, Hkv, BLOCK)).astype(np.float32)
     v["k_new"] = _normal16(rng, (B, Hkv, D))
@@ -338,7 +344,7 @@ def fill_torch(wl: Workload, device, *, chunk_rows: int = 1 << 12) -> dict[str, 
             v[nm] = t * (1.5 / 448) + (2.3 / 448)
     else:
         for nm in ("k_pool", "v_pool"):
-            v[nm] = torch.randint(-127, 128, (NB, BLOCK, Hkv, D), generator=gen,
+            v[nm] = torch.randint(-128, 128, (NB, BLOCK, Hkv, D), generator=gen,
                                   device=dev, dtype=torch.int8)
         for nm in ("k_scale", "v_scale"):
             t = torch.rand((NB, Hkv, BLOCK), generator=gen, device=dev, dtype=torch.float32)
@@ -353,6 +359,48 @@ def fill_torch(wl: Workload, device, *, chunk_rows: int = 1 << 12) -> dict[str, 
         else:
             v["k_scale"].permute(0, 2, 1)[bad] = float("nan")
             v["v_scale"].permute(0, 2, 1)[bad] = float("nan")
+    wl.values = v
+    return v
+
+
+def fill_source_numpy(wl: Workload) -> dict[str, np.ndarray]:
+    """Source mode, on the host: fp16 N(0,1) q, k_src, v_src ([num_blocks,
+    16, kv_heads, head_dim], every slot), k_new, v_new.  No codes or scales:
+    the caller quantises k_src / v_src."""
+    rng = np.random.default_rng(wl.seed + 7919)
+    B, Hq, Hkv, D, NB = wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim, wl.num_blocks
+    v = {"q": _normal16(rng, (B, Hq, D)),
+         "k_src": _normal16(rng, (NB, BLOCK, Hkv, D)),
+         "v_src": _normal16(rng, (NB, BLOCK, Hkv, D)),
+         "k_new": _normal16(rng, (B, Hkv, D)),
+         "v_new": _normal16(rng, (B, Hkv, D))}
+    wl.values = v
+    return v
+
+
+def fill_source_torch(wl: Workload, device, *, chunk_rows: int = 1 << 12) -> dict[str, Any]:
+    """Source mode on `device` with a seeded torch.Generator: the tensors of
+    fill_source_numpy (values differ from numpy's)."""
+    import torch
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed + 7919)
+    B, Hq, Hkv, D, NB = wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim, wl.num_blocks
+
+    def normal16(shape):
+        out = torch.empty(shape, dtype=torch.float16, device=dev)
+        flat = out.view(shape[0], -1)
+        for i in range(0, shape[0], chunk_rows):
+            j = min(shape[0], i + chunk_rows)
+            flat[i:j] = torch.randn((j - i, flat.shape[1]), generator=gen,
+                                    device=dev, dtype=torch.float32).to(torch.float16)
+        return out
+
+    v = {"q": normal16((B, Hq, D)),
+         "k_src": normal16((NB, BLOCK, Hkv, D)),
+         "v_src": normal16((NB, BLOCK, Hkv, D)),
+         "k_new": normal16((B, Hkv, D)),
+         "v_new": normal16((B, Hkv, D))}
     wl.values = v
     return v
 
