@@ -7,25 +7,37 @@ One step = one pass of the hot path over one batch: the KV write of each
 sequence's new token into its slot (fp16 copy, or quantising int8 / FP8 write),
 then paged decode attention over every sequence's context (split-K partition
 kernel, plus the log-sum-exp merge when the context spans several
-partitions).  Inputs are seeded synthetic tensors already resident in HBM.
+partitions).  Inputs are seeded synthetic tensors already resident in HBM;
+the 8-bit long-context caches are quantised on the device from fp16 N(0,1)
+sources by the library's own quantising write, before anything is timed.
 
 Headline workload: one Llama2-7B-shaped layer - 32 sequences x 4096 tokens,
 32 query / 32 kv heads, head_dim 128, fp16, 16-token blocks, block tables 85 %
 contiguous.  metric value = ideal KV bytes / step time (GB/s); the other
 workloads are measured the same way and reported under "others"; the
 shared-prefix workload is measured twice, through pa_decode and through the
-shared-prefix entry point (whose "decode call" time covers its three
-kernels).  "cold" repeats steps one at a time with L2 and MALL flushed first.
+shared-prefix entry point (whose "decode call" covers both its launches).
 
-"roofline" describes the dominant kernel (the decode partition kernel):
-achieved = its algorithmic bytes (the KV bytes it must read) / its mean
-duration, timed with HIP events recorded on the stream it runs on, around
-the launch of every fifth timed step (--event-every; an event is a marker in
-the stream and costs the step a few microseconds, so the other steps run
-without).  "traffic" comes from rocprofv3 counter
-summaries committed under profiles/ and is null unless they were taken on
-the current kernel source.  "cpu_baseline" times the fp64 CPU oracle on a
-bounded sample of the same workload.
+Timing protocol, per workload:
+  settle   the step runs back to back, untimed, for --settle-ms (after an
+           idle spell the GPU's clocks take some milliseconds of sustained
+           load to settle; the 128K int8 kernel runs about 25 % slower until
+           they have);
+  warm-up  W steps, untimed;
+  steps    K steps back to back between two events (ms_per_step is the host
+           wall time over them, synchronised on both sides);
+  block    the decode partition kernel alone, --block-launches back-to-back
+           launches between two events on its stream, three times: their
+           mean launch time gives "roofline.achieved" and the
+           decode_kernel_* figures;
+  cold     --cold-steps steps one at a time, L2 and MALL flushed first by
+           reading a 1 GiB buffer (outside the events).
+"paging" re-times the decode kernel of the Llama2-7B and 128K int8 workloads
+with identity, 85 %-contiguous and fully shuffled block tables (same pools,
+alternating), against the paging cost the pages report.
+"traffic" comes from rocprofv3 counter summaries committed under profiles/
+and is null unless they were taken on the current kernel source.
+"cpu_baseline" times the fp64 CPU oracle over the host's cores.
 """
 from __future__ import annotations
 
@@ -45,6 +57,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "paged-attn decode: achieved KV HBM GB/s (% of peak) and sequences/s per layer"
 HEADLINE = "llama2_7b"
 OTHERS = ["gqa70b_mixed", "prefix_shared", "long128k_int8", "long128k_fp8", "tiny_gqa"]
+PAGING = ["llama2_7b", "long128k_int8"]
+WAVE_TARGET = 2048             # the library's wave target (pa.h, balanced chunks)
 
 
 def parse():
@@ -55,17 +69,23 @@ def parse():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--others", default=",".join(OTHERS),
                     help="comma list of extra workloads to report ('' for none)")
+    ap.add_argument("--paging", default=",".join(PAGING),
+                    help="workloads whose decode is re-timed with identity, 85/15 and "
+                         "shuffled block tables ('' for none)")
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="override the partition size (-1: the workload's own choice)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="untimed back-to-back steps before each workload's warm-up")
+    ap.add_argument("--block-launches", type=int, default=50,
+                    help="back-to-back decode launches per timed block (three blocks)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="time budget of the CPU-oracle sample")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (0: the host's CPUs, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="run the workload through the shared-prefix entry point "
                          "(workloads with a shared prefix only)")
-    ap.add_argument("--event-every", type=int, default=5,
-                    help="bracket the decode kernel of every N-th timed step with HIP events "
-                         "(the kernel mean comes from those launches)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed one by one with L2 and MALL flushed before "
                          "each (reported under 'cold'; 0 to skip)")
@@ -98,15 +118,23 @@ def decode_kernel_name(wl) -> str:
     return "decode_valu_kernel" if wl.q_heads // wl.kv_heads <= 2 else "decode_mfma_kernel"
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 class Case:
     """Device-resident inputs of one workload plus its step."""
 
     def __init__(self, pa, torch, gen, name, partition_size, dev, shared_prefix=0):
-        self.pa, self.torch, self.name = pa, torch, name
+        self.pa, self.torch, self.gen, self.name = pa, torch, gen, name
         self.shared_prefix = shared_prefix          # > 0: shared-prefix path, prefix tokens
         wl = gen.make(name, poison=False)
         self.wl = wl
-        vals = gen.fill_torch(wl, dev)
+        self.q8 = wl.kv_dtype in ("int8", "fp8")             # 8-bit codes + scales
+        if self.q8:
+            vals = self._quantised_from_source(dev)
+        else:
+            vals = gen.fill_torch(wl, dev)
         self.v = vals
         self.bt = torch.from_numpy(wl.block_table).to(dev)
         self.cl = torch.from_numpy(wl.context_lens).to(dev)
@@ -123,9 +151,32 @@ class Case:
                                                    shared_prefix)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         self.out = torch.empty_like(vals["q"])
-        self.q8 = wl.kv_dtype in ("int8", "fp8")             # 8-bit codes + scales
         self.kv_bytes = gen.kv_ideal_bytes(wl)                # unique bytes
         self.kv_bytes_logical = gen.kv_ideal_bytes(wl, unique=False)
+
+    def _quantised_from_source(self, dev):
+        """The 8-bit cache as configured: fp16 N(0,1) K / V for every slot,
+        quantised per (token, kv head) by the library's quantising write."""
+        torch, wl = self.torch, self.wl
+        src = self.gen.fill_source_torch(wl, dev)
+        NB, Hkv, D = wl.num_blocks, wl.kv_heads, wl.head_dim
+        code = torch.int8 if wl.kv_dtype == "int8" else torch.uint8
+        v = {"q": src["q"], "k_new": src["k_new"], "v_new": src["v_new"]}
+        v["k_pool"] = torch.empty((NB, 16, Hkv, D), dtype=code, device=dev)
+        v["v_pool"] = torch.empty_like(v["k_pool"])
+        v["k_scale"] = torch.empty((NB, Hkv, 16), dtype=torch.float32, device=dev)
+        v["v_scale"] = torch.empty_like(v["k_scale"])
+        slots = torch.arange(NB * 16, dtype=torch.int32, device=dev)
+        write = self.pa.write_kv_int8 if wl.kv_dtype == "int8" else self.pa.write_kv_fp8
+        write(src["k_src"].view(NB * 16, Hkv, D), src["v_src"].view(NB * 16, Hkv, D), slots,
+              v["k_pool"], v["v_pool"], v["k_scale"], v["v_scale"])
+        torch.cuda.synchronize()
+        del src, slots
+        torch.cuda.empty_cache()
+        return v
+
+    def set_table(self, table):
+        self.bt = self.torch.from_numpy(table).to(self.bt.device)
 
     def write(self):
         v = self.v
@@ -141,7 +192,7 @@ class Case:
         covers the context, else the partition records."""
         v, wl = self.v, self.wl
         if self.shared_prefix:
-            # the whole entry point: suffix partition kernel, prefix kernel, merge
+            # the whole entry point: both its launches
             self.pa.decode_shared_prefix(v["q"], v["k_pool"], v["v_pool"], self.bt, self.cl,
                                          self.shared_prefix, scale=wl.scale,
                                          max_context_len=wl.max_context_len, out=self.out,
@@ -169,35 +220,59 @@ class Case:
             self.pa.merge_partials(self.ws, self.cl, wl.q_heads, wl.head_dim, self.P,
                                    wl.max_context_len, out=self.out)
 
-    def run(self, steps, warmup, event_every=1):
-        """Warm-up, then `steps` timed steps.  The decode kernel of every
-        `event_every`-th timed step is bracketed by HIP events on its stream
-        (each event is a marker in the stream, and the steps between two
-        sampled ones run without them)."""
+    def step(self):
+        self.write()
+        self.decode_kernel()
+        self.merge()
+
+    def settle(self, ms, fn=None):
+        """Back-to-back untimed calls of `fn` (the step) for at least `ms`
+        milliseconds and 20 calls, in bursts of 10 between synchronisations."""
+        fn = fn or self.step
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0, n = time.perf_counter(), 0
+        while n < 20 or (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(10):
+                fn()
+            n += 10
+            torch.cuda.synchronize()
+        return n
+
+    def run(self, steps, warmup):
+        """Warm-up, then `steps` steps back to back.  Returns (host wall
+        seconds, GPU event milliseconds) over the timed steps."""
         torch = self.torch
         for _ in range(warmup):
-            self.write()
-            self.decode_kernel()
-            self.merge()
-        every = max(1, int(event_every))
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(0, steps, every)]
+            self.step()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            self.write()
-            if i % every == 0:
-                a, b = ev[i // every]
-                a.record()
-                self.decode_kernel()
-                b.record()
-            else:
-                self.decode_kernel()
-            self.merge()
+        a.record()
+        for _ in range(steps):
+            self.step()
+        b.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
-        return wall, kern_ms
+        return time.perf_counter() - t0, a.elapsed_time(b)
+
+    def decode_blocks(self, launches, blocks=3):
+        """Mean launch time (ms) of the decode partition kernel over `blocks`
+        blocks of `launches` back-to-back launches, each block between two
+        events on the kernel's stream (the binding launches on torch's
+        current stream)."""
+        torch = self.torch
+        self.decode_kernel()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(blocks):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(launches):
+                self.decode_kernel()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / launches)
+        return out
 
     def run_cold(self, steps, flush_bytes=1 << 30):
         """Steps with the caches flushed before each: a 1 GiB buffer (beyond
@@ -224,6 +299,34 @@ class Case:
         del flush
         return sorted(step_ms), sorted(kern_ms)
 
+    def split(self):
+        """What the timed launch actually runs: the library's record mode and
+        records per (sequence, head) row, read back from the workspace header
+        after one launch, and the balanced-chunk length the library's rule
+        gives for these lengths (pa.h, workspace layout)."""
+        wl = self.wl
+        if self.shared_prefix:
+            return {"mode": "shared prefix: prefix records plus suffix chunks"}
+        if self.n_part == 1:
+            return {"mode": "direct: one wave per (sequence, kv head) over the whole context",
+                    "records_per_row": 0}
+        self.decode_kernel()
+        self.torch.cuda.synchronize()
+        hdr = self.ws[:4 * (64 + wl.batch)].view(self.torch.int32).cpu().numpy()
+        lens = wl.context_lens.astype(int)
+        if hdr[0] == 1:
+            recs = [-(-int(x) // self.P) for x in lens]
+            return {"mode": "partition items", "partition_tokens": self.P,
+                    "records_per_row": {"min": min(recs), "max": max(recs)}}
+        counts = [int(c) for c, L in zip(hdr[64:64 + wl.batch], lens) if L > 0]
+        T = sum(-(-int(x) // 16) for x in lens)
+        K = max(1, WAVE_TARGET // wl.kv_heads)
+        C = max(self.P // 16, -(-T // K))
+        return {"mode": "balanced chunks", "min_chunk_tokens": self.P,
+                "chunk_tokens": 16 * C, "chunks": -(-T // C),
+                "records_per_row": {"min": min(counts), "max": max(counts),
+                                    "mean": round(sum(counts) / len(counts), 2)}}
+
 
 def cold_summary(case, steps):
     """Median and p10/p90 of cold steps (caches flushed before each)."""
@@ -245,26 +348,66 @@ def cold_summary(case, steps):
     }
 
 
-def summarize(case, wall, kern_ms, steps):
+def measure(case, steps, warmup, args):
+    """The timing protocol of the module docstring for one workload."""
     wl = case.wl
+    settled = case.settle(args.settle_ms)
+    wall, gpu_ms = case.run(steps, warmup)
+    blocks = case.decode_blocks(max(20, args.block_launches))
+    kmean = sum(blocks) / len(blocks) / 1e3
     step_s = wall / steps
-    kmean = sum(kern_ms) / len(kern_ms) / 1e3
-    med = kern_ms[len(kern_ms) // 2] / 1e3
-    return {
+    res = {
         "workload": wl.name + (" (shared-prefix path)" if case.shared_prefix else ""),
         "batch": wl.batch, "q_heads": wl.q_heads, "kv_heads": wl.kv_heads,
         "head_dim": wl.head_dim, "block_size": 16, "kv_dtype": wl.kv_dtype,
         "max_context_len": wl.max_context_len,
         "mean_context_len": round(float(wl.context_lens.mean()), 1),
-        "partition_size": case.P, "n_part": case.n_part,
+        "partition_size": case.P, "split": case.split(),
         "kv_bytes": case.kv_bytes, "kv_bytes_logical": case.kv_bytes_logical,
+        "settle_steps": settled,
         "ms_per_step": round(step_s * 1e3, 4),
+        "ms_per_step_gpu_events": round(gpu_ms / steps, 4),
         "step_GBps": round(case.kv_bytes / step_s / 1e9, 1),
         "seq_per_s": round(wl.batch / step_s, 1),
         "decode_kernel_us_mean": round(kmean * 1e6, 2),
-        "decode_kernel_us_median": round(med * 1e6, 2),
+        "decode_kernel_us_blocks": [round(x * 1e3, 2) for x in blocks],
+        "decode_kernel_launches_timed": len(blocks) * max(20, args.block_launches),
         "decode_kernel_GBps": round(case.kv_bytes / kmean / 1e9, 1),
         "decode_kernel_frac_of_peak": round(case.kv_bytes / kmean / 1e9 / PEAK_HBM_GBS, 4),
+        "decode_kernel_seq_per_s": round(wl.batch / kmean, 1),
+    }
+    res["cold"] = cold_summary(case, args.cold_steps)
+    return res
+
+
+def paging_cost(case, args, rounds=3):
+    """The decode kernel with identity, 85/15 and fully shuffled block
+    tables over the same pools, alternating.  [ATB-KV] ("显存碎片问题")
+    reports about 3-5 % cost when 10-20 % of blocks are scattered; [KV-OPT]
+    ("四、代价与权衡") puts paged attention 5-10 % behind contiguous."""
+    gen, wl = case.gen, case.wl
+    tables = {
+        "identity": gen.make(wl.name, poison=False, overrides={"scatter": 0.0}).block_table,
+        "85/15 (the workload's)": wl.block_table,
+        "fully shuffled": gen.make(wl.name, poison=False, overrides={"scatter": 1.0}).block_table,
+    }
+    times = {k: [] for k in tables}
+    for _ in range(rounds):
+        for k, tab in tables.items():
+            case.set_table(tab)
+            case.settle(args.settle_ms / 2, fn=case.decode_kernel)
+            times[k] += case.decode_blocks(max(20, args.block_launches), blocks=2)
+    case.set_table(wl.block_table)
+    mean = {k: sum(v) / len(v) * 1e3 for k, v in times.items()}
+    base = mean["identity"]
+    return {
+        "workload": wl.name,
+        "decode_kernel_us": {k: round(v, 2) for k, v in mean.items()},
+        "cost_vs_identity_pct": {k: round(100 * (v / base - 1), 2) for k, v in mean.items()},
+        "blocks_per_variant": 2 * rounds,
+        "pages_claim": "adg.csdn.net ATB KV Cache, 显存碎片问题: 80-90 % contiguous, the scattered "
+                       "10-20 % cost about 3-5 %; discosf.com KV Cache 优化与显存管理, 四、代价与权衡: "
+                       "paged attention +5-10 % over contiguous",
     }
 
 
@@ -341,35 +484,153 @@ def counters_summary(args):
     print(json.dumps(res, indent=2))
 
 
-def cpu_baseline(case, budget_s):
-    """fp64 oracle on the host: whole sequences (all heads) in order until
-    the time budget is spent; single thread (BLAS pinned to one)."""
+# --------------------------------------------------------------------------- CPU oracle
+
+_CPU = {}
+
+
+def _cpu_worker_init(path):
+    """Oracle worker process: BLAS pinned to one thread.  The workload's host
+    copy is memory-mapped from `path` (shared page cache) on first use: the
+    workers start before the GPU is touched and the arrays are written
+    later."""
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS",
+                "BLIS_NUM_THREADS"):
+        os.environ[var] = "1"                # read when numpy's BLAS loads
+    import numpy  # noqa: F401  (loaded before the limit, so the limit applies to it)
+    from threadpoolctl import threadpool_limits
+    _CPU["limit"] = threadpool_limits(limits=1)
+    _CPU["path"] = path
+
+
+def _cpu_load():
+    if "meta" in _CPU:
+        return
+    import numpy as np
+    path = _CPU["path"]
+    with open(os.path.join(path, "meta.json")) as f:
+        _CPU["meta"] = json.load(f)
+    for k in _CPU["meta"]["arrays"]:
+        _CPU[k] = np.load(os.path.join(path, k + ".npy"), mmap_mode="r")
+
+
+def _cpu_ping(_):
+    return os.getpid()
+
+
+def _cpu_unit(unit):
+    """One sequence (g None: all its query heads) or one (sequence, kv head)
+    pair (the query heads of that kv head): the oracle's rows."""
+    from oracle import ref
+    _cpu_load()
+    b, g = unit
+    m = _CPU["meta"]
+    G = m["q_heads"] // m["kv_heads"]
+    heads = range(m["q_heads"]) if g is None else range(g * G, (g + 1) * G)
+    rows = [(b, h) for h in heads]
+    t0 = time.perf_counter()
+    ref.ref_decode(_CPU["q"], _CPU["k_pool"], _CPU["v_pool"], _CPU["block_table"],
+                   _CPU["context_lens"], m["scale"], _CPU.get("k_scale"), _CPU.get("v_scale"),
+                   rows=rows)
+    return time.perf_counter() - t0
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class OraclePool:
+    """Worker processes for the CPU baseline, started before anything
+    touches the GPU (so no process is created from one that has)."""
+
+    def __init__(self, workers):
+        import multiprocessing as mp
+        import tempfile
+        from concurrent.futures import ProcessPoolExecutor
+        self.n_aff = len(os.sched_getaffinity(0))
+        self.n = workers if workers > 0 else min(self.n_aff, 16)
+        base = "/dev/shm" if os.path.isdir("/dev/shm") else None
+        self.path = tempfile.mkdtemp(prefix="pa_oracle_", dir=base)
+        self.ex = ProcessPoolExecutor(max_workers=self.n, mp_context=mp.get_context("spawn"),
+                                      initializer=_cpu_worker_init, initargs=(self.path,))
+        list(self.ex.map(_cpu_ping, range(self.n)))
+        self.started = len(self.ex._processes)
+
+    def close(self):
+        import shutil
+        self.ex.shutdown(wait=True)
+        shutil.rmtree(self.path, ignore_errors=True)
+
+
+def cpu_baseline(case, budget_s, pool, gen):
+    """fp64 oracle on the host cores: (sequence, kv head) pairs spread over
+    the worker processes (BLAS pinned to one thread each), pairs in order
+    until the time budget is spent; plus the tiny workload on one core."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import ref
-    wl = case.wl
-    v = case.v
-    host = {k: v[k].cpu().numpy() for k in ("q", "k_pool", "v_pool")}
-    ks = v["k_scale"].cpu().numpy() if case.q8 else None
-    vs = v["v_scale"].cpu().numpy() if case.q8 else None
-    done_bytes, done_seqs = 0, 0
+    wl, v = case.wl, case.v
+    arrays = {k: v[k].cpu().numpy() for k in ("q", "k_pool", "v_pool")}
+    if case.q8:
+        arrays["k_scale"] = v["k_scale"].cpu().numpy()
+        arrays["v_scale"] = v["v_scale"].cpu().numpy()
+    arrays["block_table"] = wl.block_table
+    arrays["context_lens"] = wl.context_lens
+    for k, a in arrays.items():
+        np.save(os.path.join(pool.path, k + ".npy"), a)
+    with open(os.path.join(pool.path, "meta.json"), "w") as f:
+        json.dump({"arrays": list(arrays), "q_heads": wl.q_heads, "kv_heads": wl.kv_heads,
+                   "scale": wl.scale}, f)
+    del arrays
+    n = pool.n
+    # Whole sequences when there are enough of them: the cache interleaves
+    # the kv heads of a token, so a sequence's pages are then mapped by one
+    # worker only.
+    if wl.batch >= n:
+        units = [(b, None) for b in range(wl.batch)]
+    else:
+        units = [(b, g) for b in range(wl.batch) for g in range(wl.kv_heads)]
     per_tok = case.kv_bytes_logical / max(1, int(wl.context_lens.sum()))
+    share = 1.0 if wl.batch >= n else 1.0 / wl.kv_heads
+    list(pool.ex.map(_cpu_unit, [units[0]] * (2 * n)))     # every worker maps the arrays
+    t0 = time.perf_counter()
+    done, busy = [], 0.0
+    for i in range(0, len(units), 4 * n):
+        batch = units[i:i + 4 * n]
+        busy += sum(pool.ex.map(_cpu_unit, batch))
+        done += batch
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    done_bytes = sum(int(wl.context_lens[b]) for b, _ in done) * per_tok * share
+    seqs = len(done) * share
+    # single core, the tiny workload
+    tiny = gen.make("tiny_gqa")
+    tv = gen.fill_numpy(tiny)
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for b in range(wl.batch):
-            rows = [(b, h) for h in range(wl.q_heads)]
-            ref.ref_decode(host["q"], host["k_pool"], host["v_pool"], wl.block_table,
-                           wl.context_lens, wl.scale, ks, vs, rows=rows)
-            done_seqs += 1
-            done_bytes += int(wl.context_lens[b]) * per_tok
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "seq_per_s": round(done_seqs / dt, 3),
-            "sample": f"{done_seqs} of {wl.batch} sequences of {wl.name} (all "
-                      f"{wl.q_heads} heads each), fp64 numpy, one thread, {dt:.1f} s"}
+        reps, t1 = 0, time.perf_counter()
+        while reps < 20 or time.perf_counter() - t1 < 0.5:
+            ref.ref_decode(tv["q"], tv["k_pool"], tv["v_pool"], tiny.block_table,
+                           tiny.context_lens, tiny.scale)
+            reps += 1
+        tiny_ms = (time.perf_counter() - t1) / reps * 1e3
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": n,
+            "kind": "oracle", "seq_per_s": round(seqs / dt, 3),
+            "cpu_model": _cpu_model(), "host_cpus_in_affinity": pool.n_aff,
+            "worker_processes": pool.started,
+            "cpu_seconds_busy": round(busy, 2),
+            "single_core_tiny_gqa_ms": round(tiny_ms, 3),
+            "sample": f"{seqs:g} of {wl.batch} sequences of {wl.name} (every query head), "
+                      f"fp64 numpy oracle in {n} worker processes (BLAS one thread each), "
+                      f"{dt:.2f} s wall"}
 
 
 def main():
@@ -381,6 +642,17 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path runs on a single device)", file=sys.stderr)
         sys.exit(2)
+    pool = None
+    if not args.no_cpu_baseline and not args.copy_calibration:
+        pool = OraclePool(args.cpu_workers)      # before anything touches the GPU
+    try:
+        run_bench(args, pool)
+    finally:
+        if pool is not None:
+            pool.close()
+
+
+def run_bench(args, pool):
     import torch
 
     if args.copy_calibration:
@@ -402,41 +674,43 @@ def main():
     if args.shared_prefix and not pre:
         raise SystemExit(f"--shared-prefix: workload {args.workload} has no shared prefix")
     head = Case(pa, torch, gen, args.workload, args.partition_size, dev, shared_prefix=pre)
-    wall, kern = head.run(args.steps, args.warmup, args.event_every)
-    s = summarize(head, wall, kern, args.steps)
-    s["cold"] = cold_summary(head, args.cold_steps)
-    print(f"[bench] {args.workload}: {s['ms_per_step']} ms/step, decode kernel "
-          f"{s['decode_kernel_us_mean']} us = {s['decode_kernel_GBps']} GB/s", file=sys.stderr,
-          flush=True)
+    s = measure(head, args.steps, args.warmup, args)
+    log(f"{args.workload}: {s['ms_per_step']} ms/step, decode kernel "
+        f"{s['decode_kernel_us_mean']} us = {s['decode_kernel_GBps']} GB/s")
     if s["cold"]:
-        print(f"[bench] {args.workload} cold: step {s['cold']['step_us_median']} us, decode "
-              f"kernel {s['cold']['decode_kernel_us_median']} us = "
-              f"{s['cold']['decode_kernel_GBps']} GB/s", file=sys.stderr, flush=True)
+        log(f"{args.workload} cold: step {s['cold']['step_us_median']} us, decode "
+            f"kernel {s['cold']['decode_kernel_us_median']} us")
+    paging = []
+    names = [n for n in args.paging.split(",") if n]
+    if args.workload in names and not pre:
+        paging.append(paging_cost(head, args))
+        log(f"paging {args.workload}: {paging[-1]['cost_vs_identity_pct']}")
     others = []
+    o_steps, o_warm = max(20, args.steps // 2), max(5, args.warmup // 2)
     for name in [n for n in args.others.split(",") if n and n != args.workload]:
         c = Case(pa, torch, gen, name, -1, dev)
-        w2, k2 = c.run(max(20, args.steps // 2), max(5, args.warmup // 2), args.event_every)
-        o = summarize(c, w2, k2, max(20, args.steps // 2))
-        o["cold"] = cold_summary(c, args.cold_steps)
+        o = measure(c, o_steps, o_warm, args)
         others.append(o)
-        print(f"[bench] {name}: {o['ms_per_step']} ms/step, decode kernel "
-              f"{o['decode_kernel_us_mean']} us = {o['decode_kernel_GBps']} GB/s",
-              file=sys.stderr, flush=True)
+        log(f"{name}: {o['ms_per_step']} ms/step, decode kernel {o['decode_kernel_us_mean']} "
+            f"us = {o['decode_kernel_GBps']} GB/s")
+        if name in names:
+            paging.append(paging_cost(c, args))
+            log(f"paging {name}: {paging[-1]['cost_vs_identity_pct']}")
         del c
         torch.cuda.empty_cache()
         if name == "prefix_shared":
             # the same workload through the shared-prefix entry point
             c = Case(pa, torch, gen, name, -1, dev, shared_prefix=gen.SPECS[name]["prefix"])
-            w2, k2 = c.run(max(20, args.steps // 2), max(5, args.warmup // 2), args.event_every)
-            o = summarize(c, w2, k2, max(20, args.steps // 2))
-            o["cold"] = cold_summary(c, args.cold_steps)
+            o = measure(c, o_steps, o_warm, args)
             others.append(o)
-            print(f"[bench] {o['workload']}: {o['ms_per_step']} ms/step, decode call "
-                  f"{o['decode_kernel_us_mean']} us = {o['decode_kernel_GBps']} GB/s",
-                  file=sys.stderr, flush=True)
+            log(f"{o['workload']}: {o['ms_per_step']} ms/step, decode call "
+                f"{o['decode_kernel_us_mean']} us = {o['decode_kernel_GBps']} GB/s")
             del c
             torch.cuda.empty_cache()
-    cpu = None if args.no_cpu_baseline else cpu_baseline(head, args.cpu_seconds)
+    cpu = None
+    if pool is not None:
+        cpu = cpu_baseline(head, args.cpu_seconds, pool, gen)
+        log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} cores")
     achieved = s["decode_kernel_GBps"]
     line = {
         "metric": METRIC,
@@ -451,22 +725,27 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "accumulate": "f32",
-        "data": "synthetic (seeded N(0,1) fp16 K/V/Q; block tables per workload recipe)",
+        "data": "synthetic (seeded N(0,1) fp16 Q/K/V; 8-bit caches quantised on the device "
+                "from fp16 N(0,1) sources; block tables per workload recipe)",
         "pct_of_peak": round(100 * s["step_GBps"] / PEAK_HBM_GBS, 2),
         "seq_per_s": s["seq_per_s"],
         "config": {k: s[k] for k in ("workload", "batch", "q_heads", "kv_heads", "head_dim",
                                      "block_size", "kv_dtype", "max_context_len",
-                                     "partition_size", "n_part", "kv_bytes")},
+                                     "partition_size", "split", "kv_bytes")},
         "roofline": {"bound": "hbm", "kernel": decode_kernel_name(head.wl),
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes_per_launch": s["kv_bytes"],
                      "launch_us_mean": s["decode_kernel_us_mean"],
-                     "launches_timed": len(kern),
+                     "launches_timed": s["decode_kernel_launches_timed"],
                      "traffic": traffic_for(args.workload),
                      "source_hash": source_hash()},
+        "timing": {"settle_ms": args.settle_ms, "settle_steps": s["settle_steps"],
+                   "ms_per_step_gpu_events": s["ms_per_step_gpu_events"],
+                   "decode_kernel_us_blocks": s["decode_kernel_us_blocks"]},
         "cold": s["cold"],
         "cpu_baseline": cpu,
+        "paging": paging,
         "others": others,
     }
     print(json.dumps(line), flush=True)
