@@ -43,8 +43,9 @@
  *     surface at the caller's next synchronisation, as in HIP.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = null stream) and
  *     is asynchronous.  The library allocates no memory, keeps no state
- *     between calls and retains no pointer after it returns.  Nothing
- *     throws or aborts across this ABI.
+ *     between calls and retains no pointer after it returns (the one
+ *     exception: pa_decode_noalloc's per-device scratch array, below).
+ *     Nothing throws or aborts across this ABI.
  *   - Caller contracts that are not checked on the host (they would need a
  *     device synchronisation): 0 <= block_table[b][j] < num_blocks for
  *     j < ceil(L_b / 16); 0 <= L_b <= max_context_len.  The kernels check
@@ -176,10 +177,12 @@ int pa_decode_partition_size(int batch, int q_heads, int kv_heads, int head_dim,
                              int max_context_len, int partition_size);
 
 /*
- * Bytes of device workspace pa_decode / pa_decode_int8 need for these
- * shapes (0 when the whole context fits one partition).  The same shapes
- * give the partial records pa_decode_partials writes.  Returns 0 on
- * invalid arguments as well.
+ * Bytes of device workspace pa_decode / pa_decode_int8 / pa_decode_fp8 and
+ * pa_decode_partials* need for these shapes: the layout of the partial
+ * records (below) for ceil(max_context_len / P) partitions, P the resolved
+ * partition size.  When that is one partition, pa_decode* run in direct
+ * mode and read no workspace (NULL is accepted); pa_decode_partials* still
+ * write records.  Returns 0 on invalid arguments.
  */
 size_t pa_decode_workspace_size(int batch, int q_heads, int kv_heads, int head_dim,
                                 int max_context_len, int partition_size);
@@ -236,6 +239,33 @@ int pa_decode_fp8(void* out, float* lse_out, const void* q, const uint8_t* k_poo
                   int max_context_len, int batch, int q_heads, int kv_heads, int head_dim,
                   int block_size, int num_blocks, float scale, int partition_size,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  Same arguments, results and status
+ * codes as pa_decode (fp16 caches), minus workspace / workspace_bytes; the
+ * same kernels run.  The split-K records go to a device array inside the
+ * library (one per device, PA_NOALLOC_SCRATCH_BYTES, held from the first
+ * call on that device until the process ends).  Nothing is allocated: no
+ * hipMalloc, no hipFree, no allocating library routine.
+ *   - Shapes whose records need more than PA_NOALLOC_SCRATCH_BYTES
+ *     (pa_decode_workspace_size with the same arguments) return
+ *     PA_ERR_WORKSPACE before anything touches the device.
+ *   - Every call on one device shares that device's array, which keeps the
+ *     last call's records: calls that overlap on one device (concurrent
+ *     streams, or threads) race and must be serialised by the caller.
+ *     Calls on one stream are ordered and safe.
+ *   - The first call on each device looks up the array's device address
+ *     (PA_ERR_HIP if that fails, e.g. no device).
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int pa_decode_noalloc(void* out, float* lse_out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table, int max_blocks,
+                      const int32_t* context_lens, int max_context_len, int batch, int q_heads,
+                      int kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+                      int partition_size, void* stream);
 
 /*
  * One decode step with the KV write folded in: writes each sequence's new

@@ -13,6 +13,7 @@ Functions mirror the C entry points:
   decode(q, k_pool, v_pool, block_table, context_lens, ...)
   decode_int8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, ...)
   decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, ...)
+  decode_noalloc(q, k_pool, v_pool, block_table, context_lens, ...)
   copy_blocks(k_pool, v_pool, block_pairs, k_scale=None, v_scale=None)
 
 FP8 pools hold raw OCP E4M3 codes: torch.uint8 tensors (a torch.float8_e4m3fn
@@ -30,7 +31,7 @@ import os
 __all__ = [
     "PaError", "LIB_PATH", "lib", "status_string", "write_kv", "write_kv_int8",
     "write_kv_fp8", "partition_size", "workspace_size", "decode", "decode_int8",
-    "decode_fp8", "copy_blocks", "decode_partials",
+    "decode_fp8", "decode_noalloc", "copy_blocks", "decode_partials",
     "decode_partials_int8", "merge_partials", "decode_shared_prefix",
     "shared_prefix_workspace_size", "decode_append", "append_workspace_size", "EXPORTS",
 ]
@@ -67,6 +68,8 @@ EXPORTS = {
     "pa_decode_workspace_size": (_z, [_i, _i, _i, _i, _i, _i]),
     "pa_decode": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i,
                        _p, _z, _p]),
+    "pa_decode_noalloc": (_i, [_p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i,
+                               _f, _i, _p]),
     "pa_decode_int8": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
                             _i, _f, _i, _p, _z, _p]),
     "pa_decode_fp8": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
@@ -317,6 +320,27 @@ def decode(q, k_pool, v_pool, block_table, context_lens, scale=None, partition_s
     _check(lib.pa_decode(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                          _ptr(block_table), MB, _ptr(context_lens), L, B, Hq, Hkv, D, bs, NB,
                          scale, partition_size, _ptr(ws), ws.numel(), _stream(q)), "pa_decode")
+    return (out, lse) if return_lse else out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20       # PA_NOALLOC_SCRATCH_BYTES in include/pa.h
+
+
+def decode_noalloc(q, k_pool, v_pool, block_table, context_lens, scale=None, partition_size=0,
+                   max_context_len=None, out=None, return_lse=False):
+    """fp16 paged decode through pa_decode_noalloc: no workspace; the
+    library's per-device scratch array holds the split-K records (calls that
+    overlap on one device race).  Pass `out` (and keep return_lse False) for
+    a call that allocates nothing on this side either."""
+    torch = _torch()
+    B, Hq, Hkv, D, NB, bs, MB, L = _decode_args(q, k_pool, v_pool, block_table, context_lens,
+                                                torch.float16, max_context_len)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out, lse = _alloc_out(q, out, return_lse)
+    _check(lib.pa_decode_noalloc(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                 _ptr(block_table), MB, _ptr(context_lens), L, B, Hq, Hkv, D,
+                                 bs, NB, scale, partition_size, _stream(q)),
+           "pa_decode_noalloc")
     return (out, lse) if return_lse else out
 
 

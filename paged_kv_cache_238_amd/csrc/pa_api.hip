@@ -6,6 +6,8 @@
 
 #include <limits.h>
 
+#include <mutex>
+
 namespace {
 
 using pa::kBlockTokens;
@@ -94,7 +96,8 @@ bool blocks_fit(int batch, int max_context_len) {
 int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
 // Shared body of the decode entry points.  mode: 0 = full decode (direct
-// when one partition, else partials + merge), 1 = partials only.
+// when one partition, else partials + merge), 1 = partials only, 2 = check
+// the arguments only (no workspace check, no launch).
 int decode_common(int mode, void* out, float* lse_out, const void* q, const void* k_pool,
                   const void* v_pool, const float* k_scale, const float* v_scale, int kv,
                   const int32_t* block_table, int max_blocks, const int32_t* context_lens,
@@ -102,7 +105,7 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
                   int block_size, int num_blocks, float scale, int partition_size,
                   void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_pool || !v_pool || !block_table || !context_lens) return PA_ERR_NULL;
-  if (mode == 0 && !out) return PA_ERR_NULL;
+  if (mode != 1 && !out) return PA_ERR_NULL;
   if (kv != pa::kKvF16 && (!k_scale || !v_scale)) return PA_ERR_NULL;
   int st = check_decode_shapes(max_blocks, max_context_len, batch, q_heads, kv_heads, head_dim,
                                block_size, num_blocks, partition_size);
@@ -113,6 +116,7 @@ int decode_common(int mode, void* out, float* lse_out, const void* q, const void
     return PA_ERR_SHAPE;                     // 1-D grids, flattened block indices
   const bool direct = (mode == 0 && n_part == 1);
   const Records rec = record_layout(batch, q_heads, head_dim, n_part);
+  if (mode == 2) return PA_OK;
   if (!direct) {
     if (!workspace) return PA_ERR_NULL;
     if (workspace_bytes < rec.total) return PA_ERR_WORKSPACE;
@@ -441,6 +445,34 @@ int check_write(const void* k_new, const void* v_new, const int32_t* slot_mappin
   return PA_OK;
 }
 
+// Allocation-free decode (pa_decode_noalloc): the split-K records live in
+// this file-scope device array instead of a caller workspace.  Each device
+// the library runs on holds its own copy until the process ends.  In host
+// code the name `scratch` is only a host-side stand-in for the symbol, never
+// a device address: the device address comes from hipGetSymbolAddress, once
+// per device, with that device current, and only that pointer is passed on.
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+void* g_scratch[kMaxDevices];
+hipError_t g_scratch_status[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_status[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch[dev] = ptr;
+  });
+  if (g_scratch_status[dev] != hipSuccess || g_scratch[dev] == nullptr) return PA_ERR_HIP;
+  *out = g_scratch[dev];
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -453,7 +485,9 @@ const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED:
       return "PA_ERR_UNSUPPORTED: block_size must be 16, head_dim 64/128, group 1/2/4/8/16, "
              "partition_size a multiple of 16";
-    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace too small";
+    case PA_ERR_WORKSPACE:
+      return "PA_ERR_WORKSPACE: workspace too small (pa_decode_noalloc: the records need more "
+             "than its PA_NOALLOC_SCRATCH_BYTES of device scratch)";
     case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch failed";
     default: return "unknown pa_status";
   }
@@ -575,6 +609,35 @@ int pa_decode(void* out, float* lse_out, const void* q, const void* k_pool, cons
                        max_blocks, context_lens, max_context_len, batch, q_heads, kv_heads,
                        head_dim, block_size, num_blocks, scale, partition_size, workspace,
                        workspace_bytes, stream);
+}
+
+int pa_decode_noalloc(void* out, float* lse_out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table, int max_blocks,
+                      const int32_t* context_lens, int max_context_len, int batch, int q_heads,
+                      int kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+                      int partition_size, void* stream) {
+  // Argument checks and the size check come first: nothing touches the
+  // device for a call that is refused.  0 bytes: direct mode.
+  int st = decode_common(2, out, lse_out, q, k_pool, v_pool, nullptr, nullptr, pa::kKvF16,
+                         block_table, max_blocks, context_lens, max_context_len, batch, q_heads,
+                         kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
+                         nullptr, 0, stream);
+  if (st != PA_OK || batch == 0) return st;
+  // One partition covering every context: direct mode, no records.
+  const int P = resolve_partition(batch, kv_heads, max_context_len, partition_size);
+  const int n_part = num_partitions(max_context_len, P);
+  const size_t need =
+      n_part == 1 ? 0 : record_layout(batch, q_heads, head_dim, n_part).total;
+  if (need > kScratchBytes) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_of_current_device(&ws);
+    if (st != PA_OK) return st;
+  }
+  return decode_common(0, out, lse_out, q, k_pool, v_pool, nullptr, nullptr, pa::kKvF16,
+                       block_table, max_blocks, context_lens, max_context_len, batch, q_heads,
+                       kv_heads, head_dim, block_size, num_blocks, scale, partition_size, ws,
+                       need, stream);
 }
 
 int pa_decode_int8(void* out, float* lse_out, const void* q, const int8_t* k_pool,

@@ -178,3 +178,34 @@ def test_shared_prefix_workspace_size():
     # (the largest)
     assert pa.shared_prefix_workspace_size(1024, 32, 32, 64, 1024, 1024) == \
         _sp_bytes(1024, 32, 64, 1, 4)
+
+
+def dec_noalloc(**kw):
+    a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=16, cl=FAKE, mcl=100,
+             B=2, Hq=8, Hkv=2, D=128, bs=16, NB=64, scale=0.1, P=0)
+    a.update(kw)
+    return pa.lib.pa_decode_noalloc(a["out"], a["lse"], a["q"], a["k"], a["v"], a["bt"],
+                                    a["mb"], a["cl"], a["mcl"], a["B"], a["Hq"], a["Hkv"],
+                                    a["D"], a["bs"], a["NB"], a["scale"], a["P"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(out=None), NULL), (dict(bt=None), NULL), (dict(cl=None), NULL),
+    (dict(Hq=6, Hkv=4), SHAPE), (dict(Hkv=0), SHAPE), (dict(B=-1), SHAPE), (dict(NB=0), SHAPE),
+    (dict(mcl=257), SHAPE), (dict(B=70000), SHAPE), (dict(bs=32), UNSUP), (dict(D=96), UNSUP),
+    (dict(Hq=24, Hkv=1), UNSUP), (dict(P=24), UNSUP),
+])
+def test_noalloc_validation(kw, code):
+    """The allocation-free decode rejects the arguments pa_decode rejects,
+    with the same codes, before touching the device."""
+    assert dec_noalloc(**kw) == code
+
+
+def test_noalloc_refuses_records_beyond_its_scratch():
+    # 1000 sequences x 64 heads x 4097 records (16-token partitions of 65536
+    # tokens) need far more than the 64 MiB scratch: refused on the host
+    need = pa.workspace_size(1000, 64, 4, 128, 65536, 16)
+    assert need > pa.NOALLOC_SCRATCH_BYTES
+    assert dec_noalloc(B=1000, Hq=64, Hkv=4, mcl=65536, mb=4096, NB=1 << 20, P=16) == WS
+    # an empty batch is a no-op
+    assert dec_noalloc(B=0, mcl=0) == OK
