@@ -197,10 +197,19 @@ size_t pa_decode_workspace_size(int batch, int q_heads, int kv_heads, int head_d
  *   max_context_len  host-side upper bound on context_lens (sizes the grid;
  *                    no device-to-host read); <= max_blocks * 16
  *   scale            usually 1/sqrt(head_dim)
- *   partition_size   tokens per split-K partition, multiple of 16; 0 =
- *                    library's choice (pa_decode_partition_size).  Each
- *                    partition yields (max, sum, unnormalised output) and
- *                    partitions are merged by log-sum-exp.
+ *   partition_size   granularity of the split-K work in tokens, a multiple
+ *                    of 16; 0 = library's choice (pa_decode_partition_size).
+ *                    With the balanced split (batch * kv_heads below 2048)
+ *                    it is the minimum chunk length: the blocks of all
+ *                    sequences are cut into equal chunks of at least
+ *                    partition_size tokens (C blocks, see the workspace
+ *                    layout below), one wave per chunk and kv head, and a
+ *                    chunk yields one record per sequence it reaches.  With
+ *                    batch * kv_heads at or above 2048, record r of a row
+ *                    covers exactly partition r.  Records hold (reference
+ *                    max, sum, normalised output) and are merged by
+ *                    log-sum-exp; the result does not depend on where the
+ *                    splits fall, up to rounding.
  *   workspace        device buffer of >= pa_decode_workspace_size bytes
  *                    (may be NULL when that is 0); not shared by
  *                    concurrent calls

@@ -21,6 +21,8 @@ tensor is accepted and viewed as its bytes).
   decode_partials(...), decode_partials_int8(...), merge_partials(...)
   decode_shared_prefix(q, k_pool, v_pool, block_table, context_lens, prefix_len, ...)
   workspace_size(...), partition_size(...), shared_prefix_workspace_size(...)
+  validate(block_table, context_lens, num_blocks, ...)  host check of the caller
+      contracts the kernels do not verify (contracts.py)
 """
 from __future__ import annotations
 
@@ -34,6 +36,7 @@ __all__ = [
     "decode_fp8", "decode_noalloc", "copy_blocks", "decode_partials",
     "decode_partials_int8", "merge_partials", "decode_shared_prefix",
     "shared_prefix_workspace_size", "decode_append", "append_workspace_size", "EXPORTS",
+    "validate",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -102,6 +105,8 @@ for _name, (_res, _args) in EXPORTS.items():
     _fn.argtypes = _args
 
 BLOCK_SIZE = 16
+
+from .contracts import validate  # noqa: E402  (host-side contract check)
 
 
 class PaError(RuntimeError):

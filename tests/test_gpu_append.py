@@ -65,6 +65,10 @@ def oracle_step(wl, vals, slots):
 
 
 def run_append(pa, wl, vals, P=0, table=None):
+    if table is None:
+        # each new token's slot must lie in a block only its sequence uses
+        pa.validate(wl.block_table, wl.context_lens, wl.num_blocks,
+                    max_context_len=wl.max_context_len, new_tokens=True)
     d = {name: t(x) for name, x in vals.items()}
     bt = t(wl.block_table if table is None else table)
     cl = t(wl.context_lens)

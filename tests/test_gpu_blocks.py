@@ -69,6 +69,9 @@ def test_multi_step_copy_on_write_scenario(pa, seed, G):
     dk, dv = t(kp), t(vp)
     n_copy = 0
     for i, st in enumerate(sc.steps):
+        # contracts of the step: copy pairs, then writes into private blocks only
+        pa.validate(st.block_table, st.context_lens, sc.num_blocks, slot_mapping=st.slots,
+                    new_tokens=True, copy_pairs=st.pairs if len(st.pairs) else None)
         if len(st.pairs):
             pa.copy_blocks(dk, dv, t(st.pairs))
             kp, vp, _, _ = ref.ref_copy_blocks(kp, vp, st.pairs)
