@@ -89,6 +89,9 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed one by one with L2 and MALL flushed before "
                          "each (reported under 'cold'; 0 to skip)")
+    ap.add_argument("--profile-launches", type=int, default=0, metavar="N",
+                    help="only set up --workload and launch its decode partition kernel N "
+                         "times after 5 untimed ones (for rocprofv3 counter passes)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the "
                          "known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -643,7 +646,7 @@ def main():
               "(the decode path runs on a single device)", file=sys.stderr)
         sys.exit(2)
     pool = None
-    if not args.no_cpu_baseline and not args.copy_calibration:
+    if not args.no_cpu_baseline and not args.copy_calibration and not args.profile_launches:
         pool = OraclePool(args.cpu_workers)      # before anything touches the GPU
     try:
         run_bench(args, pool)
@@ -674,6 +677,13 @@ def run_bench(args, pool):
     if args.shared_prefix and not pre:
         raise SystemExit(f"--shared-prefix: workload {args.workload} has no shared prefix")
     head = Case(pa, torch, gen, args.workload, args.partition_size, dev, shared_prefix=pre)
+    if args.profile_launches:
+        for _ in range(5 + args.profile_launches):
+            head.decode_kernel()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": head.wl.name, "decode_launches": 5 + args.profile_launches}),
+              flush=True)
+        return
     s = measure(head, args.steps, args.warmup, args)
     log(f"{args.workload}: {s['ms_per_step']} ms/step, decode kernel "
         f"{s['decode_kernel_us_mean']} us = {s['decode_kernel_GBps']} GB/s")

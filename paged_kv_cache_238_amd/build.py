@@ -55,9 +55,10 @@ def _common(extra: list[str] | None) -> list[str]:
             "-I", os.path.join(ROOT, "include"), "-I", CSRC, *(extra or [])]
 
 
-def commands(src: str, extra: list[str] | None = None) -> list[list[str]]:
+def commands(src: str, extra: list[str] | None = None,
+             build_dir: str = BUILD_DIR) -> list[list[str]]:
     """Device pass, then host pass, for one source file."""
-    stem = os.path.join(BUILD_DIR, os.path.splitext(src)[0])
+    stem = os.path.join(build_dir, os.path.splitext(src)[0])
     path = os.path.join(CSRC, src)
     dev = [clang(), *_common(extra), "--offload-device-only", *DEVICE_ONLY_FLAGS,
            "-c", path, "-o", stem + ".hipfb"]
@@ -67,8 +68,8 @@ def commands(src: str, extra: list[str] | None = None) -> list[list[str]]:
     return [dev, host]
 
 
-def link_command(out: str) -> list[str]:
-    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+def link_command(out: str, build_dir: str = BUILD_DIR) -> list[str]:
+    objs = [os.path.join(build_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
 
 
@@ -82,11 +83,15 @@ def _run(cmd: list[str], verbose: bool) -> str:
     return res.stdout + res.stderr
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB,
+          build_dir: str = BUILD_DIR) -> str:
+    """Compile and link; `extra` compiler flags, `out` library path and
+    `build_dir` for intermediates (defaults: libpa.so next to this file,
+    _build/)."""
+    os.makedirs(build_dir, exist_ok=True)
 
     def one(src: str) -> str:
-        return "".join(_run(c, verbose) for c in commands(src, extra))
+        return "".join(_run(c, verbose) for c in commands(src, extra, build_dir))
 
     workers = max(1, min(len(SOURCES), os.cpu_count() or 1, 8))
     with ThreadPoolExecutor(max_workers=workers) as ex:
@@ -94,11 +99,21 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     for log in logs:
         if log.strip():
             sys.stderr.write(log)
-    tmp = LIB + ".tmp"
-    _run(link_command(tmp), verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = out + ".tmp"
+    _run(link_command(tmp, build_dir), verbose)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser(description="build libpa.so (gfx950)")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("-D", "--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="extra preprocessor definition (a build variant, e.g. PA_V_SWIZZLE=0)")
+    ap.add_argument("--out", default=LIB, help="library path (default: the package's libpa.so)")
+    a = ap.parse_args()
+    bdir = BUILD_DIR if not a.define else os.path.join(
+        BUILD_DIR, "variant_" + "_".join(d.replace("=", "") for d in a.define))
+    print(build(verbose=a.verbose, extra=[f"-D{d}" for d in a.define], out=os.path.abspath(a.out),
+                build_dir=bdir))

@@ -59,6 +59,11 @@ constexpr float kLn2 = 0.693147180559945309f;
 #define PA_V_ROW_PAD 16
 #endif
 constexpr int kRowPad = PA_V_ROW_PAD;   // bytes of padding per LDS row of the V tile
+// 1: the V tile's rows are unpadded and the 16-byte chunks of row r sit at
+// chunk c ^ swz(r) (see v_swizzle); 0: rows padded by kRowPad bytes.
+#ifndef PA_V_SWIZZLE
+#define PA_V_SWIZZLE 1
+#endif
 // Register sets the block loads rotate through (NBUF - 1 blocks in flight
 // while one is reduced).
 #ifndef PA_MFMA_NBUF_I8
@@ -231,7 +236,32 @@ struct Geometry {
       return 64 * ld + 16 * lg;
     }
   }
-  static constexpr int kRowBytes = D * 2 + kRowPad;   // LDS row of the fp16 V tile
+  static constexpr int kRowBytes = D * 2 + (PA_V_SWIZZLE ? 0 : kRowPad);   // LDS row of the V tile
+  // 16-byte chunks per row of the fp16 V tile.
+  static constexpr int kChunks = D * 2 / 16;
+  // Chunk c of V-tile row r is stored at chunk c ^ v_swizzle(r).  A block's
+  // V goes in as 16-byte writes (whole-line loads: the 16 lanes of one lane
+  // group write rows 0..7 at chunks c and c + 4 (fp16) or c and c + 8
+  // (int8, two writes per lane)) and comes out through ds_read_b64_tr_b16
+  // (lanes 0..31 read rows 0..7, 32 bytes each, at the same chunk pair).
+  // The table below puts the 8 rows' chunk pairs on 8 different 32-byte bank
+  // groups for the reads, and the 16 chunks of a lane group's write on 16
+  // different 16-byte bank groups, both with 64 four-byte banks served 16
+  // (writes) or 32 (reads) lanes at a time and with 32 banks served 8 or 16
+  // lanes at a time: for row r & 7 = 0..7 it is 0, 2, 12, 14, 9, 11, 5, 7
+  // (an odd low bit moves the 16-byte chunks a lane group writes to the
+  // other half of the banks), taken modulo the row's chunks.  The padded
+  // layout it replaces had two-way conflicts on every transposed read.
+  static __device__ __forceinline__ int v_swizzle(int row) {
+    if constexpr (!PA_V_SWIZZLE) return 0;
+    const int t = 2 * (row & 3) + ((row >> 2) & 1);
+    const int beta = (t & 1) ^ ((t >> 2) & 1);
+    return (t + 8 * beta) & (kChunks - 1);
+  }
+  // LDS byte address of 16-byte chunk `chunk` of V-tile row `row`.
+  static __device__ __forceinline__ uint32_t v_addr(int row, int chunk) {
+    return (uint32_t)row * kRowBytes + (uint32_t)((chunk ^ v_swizzle(row)) * 16);
+  }
 };
 
 // Scale of token 4 lg + i from a register holding, at row position p, the
@@ -317,6 +347,8 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
   const uint32_t blk_bytes = (uint32_t)kBlockTokens * row_bytes;
   // Offsets of this lane's loads within a block, and their V tile targets.
   uint32_t ld_off[NLD];
+  // V tile address of the load's (first) 16 fp16 bytes; an 8-bit load's
+  // second 16 bytes (chunk + 1 of an even chunk) sit at that address ^ 16.
   uint32_t ld_lds[NLD];
   int ld_row[NLD];
 #pragma unroll
@@ -324,15 +356,28 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
     ld_row[ld] = Geo::load_row(ld, lane);
     const int col = Geo::load_col(ld, lane);
     ld_off[ld] = (uint32_t)ld_row[ld] * row_bytes + (uint32_t)g * D * ESZ + (uint32_t)col;
-    ld_lds[ld] = (uint32_t)ld_row[ld] * Geo::kRowBytes + (uint32_t)(col / ESZ) * 2;
+    const int chunk = (col / ESZ) * 2 / 16;          // 16-byte chunk of the fp16 row
+    ld_lds[ld] = Geo::v_addr(ld_row[ld], chunk);
   }
   const char* kbase = static_cast<const char*>(p.k_pool);
   const char* vbase = static_cast<const char*>(p.v_pool);
   const uint32_t scale_blk_bytes = (uint32_t)kBlockTokens * Hkv * sizeof(float);
 
-  // LDS addresses of this lane's transposed V reads: tile nb, group lg reads
-  // token rows 4*lg + li/4 at dims 16*nb + 4*(li%4) (8 bytes each).
-  const uint32_t tr_base = (uint32_t)(4 * lg + li / 4) * Geo::kRowBytes + (uint32_t)(4 * (li % 4)) * 2;
+  // LDS addresses of this lane's transposed V reads: for tile n, group lg
+  // reads token row 4*lg + li/4 at dims 16*n + 4*(li%4) (8 bytes), i.e.
+  // chunk 2n + (li%4)/2, byte 8*(li%2) of it.  Swizzled, that chunk sits at
+  // (2n + (li%4)/2) ^ swz = 2 (n ^ (x >> 1)) + (x & 1) with x = swz ^ ((li%4)/2);
+  // the rows start at multiples of the 256- or 128-byte row, so tile n's
+  // address is tr_base ^ (32 n).
+  const uint32_t tr_base = [&] {
+    const int row = 4 * lg + li / 4;
+    if constexpr (PA_V_SWIZZLE) {
+      const int x = Geo::v_swizzle(row) ^ ((li % 4) >> 1);
+      return (uint32_t)row * Geo::kRowBytes + (uint32_t)(32 * (x >> 1) + 16 * (x & 1) + 8 * (li & 1));
+    } else {
+      return (uint32_t)row * Geo::kRowBytes + (uint32_t)(4 * (li % 4)) * 2;
+    }
+  }();
 
   do {                                       // segments of the item
   if constexpr (!PREFIX) note_record_count(p, sg, tid == 0);
@@ -521,7 +566,7 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
         else f8x16_to_h16(R.v[ld], a, c);
         if (zero_row) a = c = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(dst) = a;
-        *reinterpret_cast<uint4*>(dst + 16) = c;
+        *reinterpret_cast<uint4*>(s_tile + (ld_lds[ld] ^ 16u)) = c;
       } else {
         uint4 a = R.v[ld];
         if (zero_row) a = make_uint4(0, 0, 0, 0);
@@ -599,13 +644,18 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
       pB[i] = (_Float16)pv;
     }
 
-    // O^T += V^T P^T, V^T read transposed from LDS.
+    // O^T += V^T P^T, V^T read transposed from LDS.  (The empty asm keeps
+    // the per-tile address XORs inside the loop: hoisted, they would hold
+    // NT registers for the whole segment.)
+    uint32_t trb = tr_base;
+    if constexpr (PA_V_SWIZZLE) asm volatile("" : "+v"(trb));
     typedef __attribute__((address_space(3))) s4 lds_s4;
     const __attribute__((address_space(3))) char* tile3 =
         (const __attribute__((address_space(3))) char*)(s_tile);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(tile3 + tr_base + n * 32));
+      const uint32_t at = PA_V_SWIZZLE ? (trb ^ (uint32_t)(n * 32)) : trb + n * 32;
+      s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(tile3 + at));
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, a), pB, acc[n], 0,
                                                      0, 0);
     }
