@@ -706,55 +706,58 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
     }
   };
 
-  // Full blocks of the segment, streamed in order.  Register sets rotate so that
-  // NBUF - 1 blocks are in flight while one is reduced (int8 blocks are half
-  // the bytes, so they go one deeper); prefetches past the end read nothing.
-  // Block ids: each register set carries nid, the id of the next block it
-  // will receive, read from LDS when its current block is issued.  Every
-  // branch is wave-uniform (workgroup-uniform where it holds a barrier) and
-  // no vector load sits inside one, so the waits stay exact.
+  // The segment's blocks: the partial last block (a sequence's last segment
+  // only) first, then the full blocks in order.  Softmax does not depend on
+  // the order, and loading the partial block with the first full ones
+  // overlaps its memory latency with theirs instead of paying it again after
+  // the full blocks drain.  Register sets rotate so that NBUF - 1 blocks are
+  // in flight while one is reduced (int8 blocks are half the bytes, so they
+  // go one deeper); the partial block's set is free again before the
+  // rotation needs its last one.  Loads that have nothing to read (no
+  // partial block, prefetches past the end) use an empty buffer resource
+  // and fetch nothing, so every load is issued unconditionally.  Block ids:
+  // each register set carries nid, the id of the next block it will
+  // receive, read from LDS when its current block is issued.  Every branch
+  // is wave-uniform (workgroup-uniform where it holds a barrier) and no
+  // vector load sits inside one, so the waits stay exact.
   constexpr int NBUF = I8 ? PA_MFMA_NBUF_I8 : PA_MFMA_NBUF_F16;
   std::integral_constant<bool, false> full;
-  // Id of the partial last block, in flight while the full blocks stream.
+  // Id of the partial last block (read as 0 past the segment's slice).
   const int tail_id = (int)__builtin_amdgcn_raw_buffer_load_b32(rids, (uint32_t)nfull * 4u, 0, 0);
-  if (nfull > 0) {
-    fill_ids(0);
-    int id_base = 0;                         // id held in s_ids[0]
-    auto lds_id = [&](int j) { return s_ids[min(j - id_base, kIdCap - 1)]; };
-    Regs R[NBUF];
-    int nid[NBUF];
-    auto issue = [&](int j, int slot, int blk) {
-      load_block(blk, j < nfull, R[slot]);
-      if (j + NBUF - id_base >= kIdCap && j + NBUF < nfull) {
-        fill_ids(j + NBUF);                  // rare: segments longer than kIdCap blocks
-        id_base = j + NBUF;
-      }
-      nid[slot] = lds_id(j + NBUF);
-    };
-    // The prologue's loads stay in block order, so each block's wait
-    // counts only the blocks issued after it.
-#pragma unroll
-    for (int s = 0; s + 1 < NBUF; ++s) {
-      issue(s, s, __builtin_amdgcn_readfirstlane(lds_id(s)));
-      __builtin_amdgcn_sched_barrier(0);
+  fill_ids(0);                               // also waits for tail_id
+  int id_base = 0;                           // id held in s_ids[0]
+  auto lds_id = [&](int j) { return s_ids[min(j - id_base, kIdCap - 1)]; };
+  Regs R[NBUF];
+  int nid[NBUF];
+  auto issue = [&](int j, int slot, int blk) {
+    load_block(blk, j < nfull, R[slot]);
+    if (j + NBUF - id_base >= kIdCap && j + NBUF < nfull) {
+      fill_ids(j + NBUF);                    // rare: segments longer than kIdCap blocks
+      id_base = j + NBUF;
     }
-    nid[NBUF - 1] = lds_id(NBUF - 1);
-    for (int k = 0; k < nfull; k += NBUF) {
+    nid[slot] = lds_id(j + NBUF);
+  };
+  Regs T;
+  load_block(__builtin_amdgcn_readfirstlane(tail_id), tail > 0, T);
+  __builtin_amdgcn_sched_barrier(0);
+  // The prologue's loads stay in block order after the partial block's, so
+  // each block's wait counts only the blocks issued after it.
 #pragma unroll
-      for (int s = 0; s < NBUF; ++s) {
-        constexpr int kLast = NBUF - 1;
-        const int slot = (s + kLast) % NBUF;
-        issue(k + s + kLast, slot, __builtin_amdgcn_readfirstlane(nid[slot]));
-        __builtin_amdgcn_sched_barrier(0);
-        if (s == 0 || k + s < nfull) process_block(full, R[s], kBlockTokens);
-      }
-    }
+  for (int s = 0; s + 1 < NBUF; ++s) {
+    issue(s, s, __builtin_amdgcn_readfirstlane(lds_id(s)));
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // The partial last block (only in a sequence's last segment).
-  if (tail > 0) {
-    Regs T;
-    load_block(__builtin_amdgcn_readfirstlane(tail_id), true, T);
-    process_block(std::integral_constant<bool, true>(), T, tail);
+  nid[NBUF - 1] = lds_id(NBUF - 1);
+  if (tail > 0) process_block(std::integral_constant<bool, true>(), T, tail);
+  for (int k = 0; k < nfull; k += NBUF) {
+#pragma unroll
+    for (int s = 0; s < NBUF; ++s) {
+      constexpr int kLast = NBUF - 1;
+      const int slot = (s + kLast) % NBUF;
+      issue(k + s + kLast, slot, __builtin_amdgcn_readfirstlane(nid[slot]));
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == 0 || k + s < nfull) process_block(full, R[s], kBlockTokens);
+    }
   }
   finalize();
   } while (!PREFIX && next_segment(p, sg));
