@@ -128,10 +128,12 @@ def log(msg):
 class Case:
     """Device-resident inputs of one workload plus its step."""
 
-    def __init__(self, pa, torch, gen, name, partition_size, dev, shared_prefix=0):
+    def __init__(self, pa, torch, gen, name, partition_size, dev, shared_prefix=0,
+                 overrides=None, label=None):
         self.pa, self.torch, self.gen, self.name = pa, torch, gen, name
         self.shared_prefix = shared_prefix          # > 0: shared-prefix path, prefix tokens
-        wl = gen.make(name, poison=False)
+        self.label = label
+        wl = gen.make(name, poison=False, overrides=overrides)
         self.wl = wl
         self.q8 = wl.kv_dtype in ("int8", "fp8")             # 8-bit codes + scales
         if self.q8:
@@ -360,7 +362,8 @@ def measure(case, steps, warmup, args):
     kmean = sum(blocks) / len(blocks) / 1e3
     step_s = wall / steps
     res = {
-        "workload": wl.name + (" (shared-prefix path)" if case.shared_prefix else ""),
+        "workload": case.label or (wl.name + (" (shared-prefix path)" if case.shared_prefix
+                                               else "")),
         "batch": wl.batch, "q_heads": wl.q_heads, "kv_heads": wl.kv_heads,
         "head_dim": wl.head_dim, "block_size": 16, "kv_dtype": wl.kv_dtype,
         "max_context_len": wl.max_context_len,
@@ -706,8 +709,20 @@ def run_bench(args, pool):
         if name in names:
             paging.append(paging_cost(c, args))
             log(f"paging {name}: {paging[-1]['cost_vs_identity_pct']}")
+        mixed_len = c.wl.context_lens if name == "gqa70b_mixed" else None
         del c
         torch.cuda.empty_cache()
+        if mixed_len is not None:
+            # the same batch and bytes at one uniform length: what mixed lengths cost
+            L = int(round(float(mixed_len.mean())))
+            c = Case(pa, torch, gen, name, -1, dev, overrides={"lmin": L, "lmax": L},
+                     label=f"gqa70b_mixed uniform-length twin ({L} tokens each)")
+            o = measure(c, o_steps, o_warm, args)
+            others.append(o)
+            log(f"{o['workload']}: decode kernel {o['decode_kernel_us_mean']} us = "
+                f"{o['decode_kernel_GBps']} GB/s")
+            del c
+            torch.cuda.empty_cache()
         if name == "prefix_shared":
             # the same workload through the shared-prefix entry point
             c = Case(pa, torch, gen, name, -1, dev, shared_prefix=gen.SPECS[name]["prefix"])

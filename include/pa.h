@@ -421,7 +421,7 @@ int pa_merge_partials(void* out, float* lse_out, const int32_t* context_lens,
  * head g, the G query heads of every sequence) form 16-query tiles against
  * the shared keys on the matrix cores, giving one (max, sum, output) record
  * per (sequence, query head, prefix partition) - partitions of 16 to 256
- * tokens, sized so that the prefix kernel runs about 1024 waves; the private
+ * tokens, sized so that the prefix work runs about 512 waves; the private
  * suffixes [prefix_len, L_b) are decoded as by pa_decode_partials; one
  * log-sum-exp merge combines both record sets.  The result is the same
  * attention as pa_decode (up to rounding order).

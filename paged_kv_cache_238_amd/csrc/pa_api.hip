@@ -188,12 +188,16 @@ PrefixRecords prefix_layout(int batch, int q_heads, int head_dim, int n_suf, int
   return r;
 }
 
-// Partition of the shared prefix: short enough that the prefix kernel has
+// Partition of the shared prefix: short enough that the prefix work has
 // about PA_PREFIX_WAVES waves ((query tile, partition, kv head) items), at
-// least one block, at most kRunPartition.  Its waves stream few blocks each
-// and are latency-bound, so more of them win over fewer, longer ones.
+// least one block, at most kRunPartition.  On 64 sequences sharing a
+// 1024-token prefix at 32 kv heads (4 query tiles), with the suffix work in
+// the same launch, the call took 56.1-56.3 us with 512 waves (256-token
+// partitions), 59.4-59.9 us with 1024, 59.0-59.4 us with 256 (512-token
+// partitions, the cap raised) and 83.7 us with 128; grouping the four tiles
+// of a partition on one XCD changed nothing (alternating builds, one box).
 #ifndef PA_PREFIX_WAVES
-#define PA_PREFIX_WAVES 1024
+#define PA_PREFIX_WAVES 512
 #endif
 int prefix_partition(int batch, int q_heads, int kv_heads, int prefix_len) {
   const long long tiles = ((long long)batch * (q_heads / kv_heads) + 15) / 16;

@@ -153,11 +153,11 @@ def test_shared_prefix_workspace_size():
     # suffix records: a 512-token suffix is 32 blocks, at most four
     # partitions of 8 blocks (128 tokens), so 4 of them (+1 per row); prefix
     # records: 4 query tiles x 32 kv heads = 128 waves per prefix partition,
-    # so 128-token partitions (about 1024 waves), 8 of them
+    # so 256-token partitions (about 512 waves), 4 of them
     rows = 64 * 32
     suf = 512 + rows * 5 * 8 + rows * 5 * 256
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
-        suf + rows * 8 * 8 + rows * 8 * 256
+        suf + rows * 4 * 8 + rows * 4 * 256
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
         _sp_bytes(64, 32, 128, 4, 8)
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1000) == 0
