@@ -159,21 +159,21 @@ def test_shared_prefix_workspace_size():
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
         suf + rows * 4 * 8 + rows * 4 * 256
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1024) == \
-        _sp_bytes(64, 32, 128, 4, 8)
+        _sp_bytes(64, 32, 128, 4, 4)
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1536, 1000) == 0
     # longer suffixes: 4096 - 1024 = 3072 tokens, 192 blocks; partitions of
     # 48 blocks would exceed 256 tokens, so 256 (12 partitions); prefix: one
     # query tile x 8 kv heads = 8 waves per partition, so one-block
-    # partitions, 64 of them
+    # partitions (about 512 waves), 64 of them
     assert pa.shared_prefix_workspace_size(8, 8, 8, 128, 4096, 1024) == \
         _sp_bytes(8, 8, 128, 12, 64)
     # no suffix beyond the prefix: one (empty) suffix partition
     assert pa.shared_prefix_workspace_size(64, 32, 32, 128, 1024, 1024) == \
-        _sp_bytes(64, 32, 128, 1, 8)
-    # few queries: 2 tiles x 8 kv heads = 16 waves per partition, so the
-    # smallest partition (one block), 64 of them
+        _sp_bytes(64, 32, 128, 1, 4)
+    # few queries: 2 tiles x 8 kv heads = 16 waves per partition, so
+    # 32-token partitions (two blocks), 32 of them
     assert pa.shared_prefix_workspace_size(4, 64, 8, 128, 1024, 1024) == \
-        _sp_bytes(4, 64, 128, 1, 64)
+        _sp_bytes(4, 64, 128, 1, 32)
     # many queries: 64 tiles x 32 heads = 2048 waves per partition -> 256 tokens
     # (the largest)
     assert pa.shared_prefix_workspace_size(1024, 32, 32, 64, 1024, 1024) == \
