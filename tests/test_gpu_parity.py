@@ -454,6 +454,28 @@ def test_full_size_every_row(pa, name):
     np.testing.assert_allclose(lse, want_lse, rtol=0, atol=1e-4)
 
 
+def test_record_rounding_budget_llama2(pa):
+    """The error the fp16 split-K records add, measured: the full-size
+    Llama2-7B layer split (the library's balanced chunks, two fp16 records
+    per row, merged) and in direct mode (one partition covering the
+    context, no records), both against the oracle on every row.  Both meet
+    the tolerance; the difference is what the records cost."""
+    wl = gen.make("llama2_7b", poison=True)
+    vals = gen.fill_torch(wl, DEV)
+    d = dict(vals)
+    d["block_table"] = t(wl.block_table)
+    d["context_lens"] = t(wl.context_lens)
+    host = _host_copy(wl, d)
+    want, _ = oracle_decode(wl, host)
+    errs = {}
+    for what, P in (("split, fp16 records", 0), ("direct, no records", 4096)):
+        out = gpu_decode(pa, wl, d, partition_size=P, return_lse=False).cpu().numpy()
+        check_close(out, want, f"llama2_7b {what}")
+        err = out.astype(np.float64) - want
+        errs[what] = float(np.linalg.norm(err) / np.linalg.norm(want))
+    say(f"  REPORT llama2_7b relative RMS: {errs}")
+
+
 def test_chunks_longer_than_a_partition(pa):
     """A long context in a small batch with a forced 16-token partition: the
     balanced chunks are several partitions long (one wave merges them

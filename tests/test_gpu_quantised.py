@@ -155,8 +155,8 @@ def test_long128k_pools_bit_identical(long128k):
 
 def test_long128k_every_row_vs_oracle(pa, long128k):
     """Every (sequence, query head) row of the full-size 128K decode, in the
-    benchmark's launch configuration (512-token partitions), against the
-    oracle on its own quantised cache."""
+    benchmark's launch configuration (partition_size 512: balanced chunks of
+    at least 512 tokens), against the oracle on its own quantised cache."""
     b = long128k
     assert b.identical is True, b.identical
     wl = b.wl
@@ -182,6 +182,26 @@ def test_long128k_quantisation_error_report(pa, long128k):
     assert np.isfinite(out).all()
     rel = report(out, src_ref, f"long128k {b.kind} GPU vs oracle on the fp16 source")
     assert rel < 0.1
+
+
+def test_long128k_record_rounding_budget(pa, long128k):
+    """The error the fp16 split-K records add on the 128K workload: the
+    benchmark's launch (512-token minimum chunks, 64 fp16 records per row,
+    merged) against direct mode (one wave per (sequence, kv head) over the
+    whole 131072 tokens, no records), both against the oracle on every row.
+    The matrix-core kernel's fp16 probabilities are in both."""
+    b = long128k
+    assert b.identical is True, b.identical
+    wl = b.wl
+    want, _ = ref.ref_decode(b.q_host, b.host[0], b.host[1], wl.block_table, wl.context_lens,
+                             wl.scale, b.host[2], b.host[3])
+    errs = {}
+    for what, P in (("split, fp16 records", wl.partition_size), ("direct, no records", 131072)):
+        out = decode(pa, wl, b.q, b.dev, b.bt, b.cl, P)[0].cpu().numpy()
+        check_close(out, want, f"long128k {b.kind} {what}")
+        err = out.astype(np.float64) - want
+        errs[what] = float(np.linalg.norm(err) / np.linalg.norm(want))
+    say(f"  REPORT long128k {b.kind} relative RMS: {errs}")
 
 
 # --------------------------------------------------------------------------- small shapes
