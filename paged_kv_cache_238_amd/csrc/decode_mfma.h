@@ -323,19 +323,33 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
   const int groups = Hkv / wpg;
   Segment sg;
   int tile = 0;
+  int g_prefix = 0;
   if constexpr (PREFIX) {
-    const int n_rg = p.n_part * groups;
-    tile = wg / n_rg;
-    const int part = (wg % n_rg) / groups;
-    sg = Segment{0, -1, part * (p.partition_size / kBlockTokens),
-                 p.partition_size / kBlockTokens, part, (int)(wg % groups), 0, 0, -1, 0};
+    if (p.prefix_tile_waves) {
+      // item = (tile group, partition, kv head), kv heads fastest; wave w
+      // takes query tile tile_group * wpg + w (a tile past the last one has
+      // only padding slots and stores nothing)
+      const int n_ph = p.n_part * Hkv;
+      tile = (wg / n_ph) * wpg + w;
+      const int part = (wg % n_ph) / Hkv;
+      g_prefix = wg % Hkv;
+      sg = Segment{0, -1, part * (p.partition_size / kBlockTokens),
+                   p.partition_size / kBlockTokens, part, 0, 0, 0, -1, 0};
+    } else {
+      const int n_rg = p.n_part * groups;
+      tile = wg / n_rg;
+      const int part = (wg % n_rg) / groups;
+      sg = Segment{0, -1, part * (p.partition_size / kBlockTokens),
+                   p.partition_size / kBlockTokens, part, (int)(wg % groups), 0, 0, -1, 0};
+      g_prefix = sg.grp * wpg + w;
+    }
   } else {
     sg = locate_work(p, groups, wg);
     if (!p.direct && wg == 0 && tid == 0)
       p.header[0] = (long long)p.batch * Hkv >= p.target_waves ? 1 : 0;
     if (sg.b < 0) return;                    // no work for this workgroup
   }
-  const int g = sg.grp * wpg + w;
+  const int g = PREFIX ? g_prefix : sg.grp * wpg + w;
   const int h0 = g * G;
 
   char* s_tile = smem + w * TILE;            // this wave's V tile

@@ -70,6 +70,9 @@ struct DecodeParams {
   // query slots of a wave are queries of different sequences: query
   // qi = tile * 16 + slot is head g * G + qi % G of sequence qi / G.
   int prefix_tiles;           // ceil(batch * G / 16)
+  int prefix_tile_waves;      // 1: the waves of a prefix workgroup are consecutive
+                              // query tiles of one kv head (they stream the same
+                              // K/V lines together); 0: kv heads of one tile
 };
 
 struct MergeParams {
