@@ -502,7 +502,10 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
 
   // Loads of one block.  real == false: a prefetch past the end; its
   // resource is empty, so the loads return zeros without touching memory.
-  auto load_block = [&](int blk, bool real, Regs& R) {
+  // Rows at or past `rows` (the partial last block) are read at an offset
+  // past the resource's end, which likewise returns zeros without a memory
+  // access; they are masked out anyway.
+  auto load_block = [&](int blk, bool real, int rows, Regs& R) {
     if ((unsigned)blk >= (unsigned)p.num_blocks) {
       if (real) bad_blk = true;              // the record becomes NaN
       real = false;
@@ -511,10 +514,13 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
     const uint32_t nbytes = real ? blk_bytes : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)blk * blk_bytes, nbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)blk * blk_bytes, nbytes);
+    uint32_t off[NLD];
 #pragma unroll
-    for (int ld = 0; ld < NLD; ++ld) R.k[ld] = buffer_load16_kv<kLineNT>(rk, ld_off[ld]);
+    for (int ld = 0; ld < NLD; ++ld) off[ld] = ld_row[ld] < rows ? ld_off[ld] : blk_bytes;
 #pragma unroll
-    for (int ld = 0; ld < NLD; ++ld) R.v[ld] = buffer_load16_kv<kLineNT>(rv, ld_off[ld]);
+    for (int ld = 0; ld < NLD; ++ld) R.k[ld] = buffer_load16_kv<kLineNT>(rk, off[ld]);
+#pragma unroll
+    for (int ld = 0; ld < NLD; ++ld) R.v[ld] = buffer_load16_kv<kLineNT>(rv, off[ld]);
     if constexpr (I8) {
       // scales [NB, Hkv, 16] of kv head g: one float per lane, rotated by
       // 4 lg within each row of 16 lanes so that the four tokens 4 lg .. 4 lg+3
@@ -744,7 +750,7 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
   Regs R[NBUF];
   int nid[NBUF];
   auto issue = [&](int j, int slot, int blk) {
-    load_block(blk, j < nfull, R[slot]);
+    load_block(blk, j < nfull, kBlockTokens, R[slot]);
     if (j + NBUF - id_base >= kIdCap && j + NBUF < nfull) {
       fill_ids(j + NBUF);                    // rare: segments longer than kIdCap blocks
       id_base = j + NBUF;
@@ -752,7 +758,7 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
     nid[slot] = lds_id(j + NBUF);
   };
   Regs T;
-  load_block(__builtin_amdgcn_readfirstlane(tail_id), tail > 0, T);
+  load_block(__builtin_amdgcn_readfirstlane(tail_id), tail > 0, tail, T);
   __builtin_amdgcn_sched_barrier(0);
   // The prologue's loads stay in block order after the partial block's, so
   // each block's wait counts only the blocks issued after it.

@@ -278,8 +278,12 @@ __device__ __forceinline__ void valu_body(const DecodeParams& p, const int wg) {
 
   // Every K load of a block, then every V load (V arrives while the scores
   // are computed).  real == false: a prefetch past the end; its resource is
-  // empty, so the loads return zeros without touching memory.
-  auto load_block = [&](int blk, bool real, Regs& R) {
+  // empty, so the loads return zeros without touching memory.  Rows at or
+  // past `rows` (the partial last block) are read at an offset past the
+  // resource's end, which likewise returns zeros without a memory access:
+  // they are masked out anyway, and on short sequences they are a few
+  // percent of the bytes.
+  auto load_block = [&](int blk, bool real, int rows, Regs& R) {
     if ((unsigned)blk >= (unsigned)p.num_blocks) {
       if (real) bad_blk = true;              // the record becomes NaN
       real = false;
@@ -288,10 +292,13 @@ __device__ __forceinline__ void valu_body(const DecodeParams& p, const int wg) {
     const uint32_t nbytes = real ? blk_bytes : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)blk * blk_bytes, nbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)blk * blk_bytes, nbytes);
+    uint32_t off[NL];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) buffer_load<NT>(R.k[i], rk, lane_off[i]);
+    for (int i = 0; i < NL; ++i) off[i] = (r + RPW * i < rows) ? lane_off[i] : blk_bytes;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) buffer_load<NT>(R.v[i], rv, lane_off[i]);
+    for (int i = 0; i < NL; ++i) buffer_load<NT>(R.k[i], rk, off[i]);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) buffer_load<NT>(R.v[i], rv, off[i]);
     if constexpr (I8) {
       const uint32_t sbytes = real ? scale_blk_bytes : 0u;
       const size_t sblk = (size_t)blk * kBlockTokens * Hkv;
@@ -449,7 +456,8 @@ __device__ __forceinline__ void valu_body(const DecodeParams& p, const int wg) {
   int next_chunk = 1;                        // chunk held in `ids_next`
   auto issue = [&](int k, Regs& R) {
     const bool real = k < nreal;
-    load_block(__builtin_amdgcn_readlane(ids, real ? (k & 63) : 0), real, R);
+    load_block(__builtin_amdgcn_readlane(ids, real ? (k & 63) : 0), real,
+               k == nfull ? tail : kBlockTokens, R);
   };
   auto done = [&](int k) {                   // block k reduced; k + NBUF is issued next
     if (((k + NBUF) & 63) == 0 && k + NBUF < nreal) {
