@@ -334,13 +334,13 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
       const int part = (wg % n_ph) / Hkv;
       g_prefix = wg % Hkv;
       sg = Segment{0, -1, part * (p.partition_size / kBlockTokens),
-                   p.partition_size / kBlockTokens, part, 0, 0, 0, -1, 0};
+                   p.partition_size / kBlockTokens, part, 0, 0, 0, -1, 0, 0};
     } else {
       const int n_rg = p.n_part * groups;
       tile = wg / n_rg;
       const int part = (wg % n_rg) / groups;
       sg = Segment{0, -1, part * (p.partition_size / kBlockTokens),
-                   p.partition_size / kBlockTokens, part, (int)(wg % groups), 0, 0, -1, 0};
+                   p.partition_size / kBlockTokens, part, (int)(wg % groups), 0, 0, -1, 0, 0};
       g_prefix = sg.grp * wpg + w;
     }
   } else {

@@ -350,20 +350,7 @@ __device__ __forceinline__ void valu_body(const DecodeParams& p, const int wg) {
         s[hh][i] = sc;
       }
     }
-    float vf[NL][8];
-    float vsc[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      kv_to_f32<KV>(R.v[i], vf[i]);
-      vsc[i] = R.vs[i];
-      if constexpr (TAIL) {
-        if (r + RPW * i >= valid) {   // masked row: value and its scale may be NaN
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vf[i][e] = 0.f;
-          vsc[i] = 0.f;
-        }
-      }
-    }
+    // Rescale by the new running max; the scores become probabilities.
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       float mb = s[hh][0];
@@ -377,13 +364,31 @@ __device__ __forceinline__ void valu_body(const DecodeParams& p, const int wg) {
       for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const float pr = fast_exp2(s[hh][i] - m_use);
-        l[hh] += pr;
-        const float pv = I8 ? pr * vsc[i] : pr;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pv, vf[i][e], acc[hh][e]);
+        s[hh][i] = fast_exp2(s[hh][i] - m_use);
+        l[hh] += s[hh][i];
       }
       m[hh] = m_new;
+    }
+    // V rows one load at a time (each converted once for all heads of the
+    // group), so only one load's values are live as fp32.
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float vf[8];
+      kv_to_f32<KV>(R.v[i], vf);
+      float vsc = R.vs[i];
+      if constexpr (TAIL) {
+        if (r + RPW * i >= valid) {   // masked row: value and its scale may be NaN
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vf[e] = 0.f;
+          vsc = 0.f;
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float pv = I8 ? s[hh][i] * vsc : s[hh][i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pv, vf[e], acc[hh][e]);
+      }
     }
   };
 

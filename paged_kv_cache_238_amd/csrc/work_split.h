@@ -54,6 +54,8 @@ struct Segment {
   int nb;     // blocks of sequence b
   int end;    // flattened end of the chunk (exclusive)
   int C;      // chunk length in blocks
+  int lane_len;   // per lane, not uniform: the length of sequence `lane`
+                  // (balanced chunks over batches of up to 64 sequences)
 };
 
 // Cross-lane steps on the VALU (DPP and gfx950's permlane swaps) rather
@@ -105,7 +107,7 @@ __device__ inline int blocks_of(const DecodeParams& p, int L) {
 // First segment of workgroup `wg` of the launch's partition work.  Must be
 // called by all 64 lanes of each wave; the result is wave-uniform.
 __device__ inline Segment locate_work(const DecodeParams& p, int groups, int wg) {
-  Segment s{-1, -1, 0, 0, 0, wg % groups, 0, 0, -1, 0};
+  Segment s{-1, -1, 0, 0, 0, wg % groups, 0, 0, -1, 0, 0};
   const int item = wg / groups;              // head groups fastest
   const int P = p.partition_size;
   if (p.direct) {                            // empty or invalid sequences included
@@ -135,6 +137,7 @@ __device__ inline Segment locate_work(const DecodeParams& p, int groups, int wg)
   if (T == 0 || item >= (T + C - 1) / C) return s;
   s.C = C;
   s.end = min(start + C, T);
+  s.lane_len = len0;
   // the sequence holding flattened block `start`: prefix sum over the lanes
   int base = 0;                              // blocks of the sequences before chunk b0
   for (int b0 = 0; b0 < p.batch; b0 += 64) {
@@ -160,7 +163,9 @@ __device__ inline Segment locate_work(const DecodeParams& p, int groups, int wg)
 }
 
 // Next segment of a balanced chunk: the following sequence with blocks, if
-// the chunk reaches it.  Wave-uniform.
+// the chunk reaches it.  Wave-uniform.  Batches of up to 64 take the length
+// from the lanes that locate_work loaded, so the switch waits on no memory
+// read before the table ids.
 __device__ inline bool next_segment(const DecodeParams& p, Segment& s) {
   if (s.end < 0) return false;
   const int F = s.F + s.nb;
@@ -168,7 +173,7 @@ __device__ inline bool next_segment(const DecodeParams& p, Segment& s) {
   int b = s.b, L = 0, nb = 0;
   while (nb == 0 && b + 1 < p.batch) {
     ++b;
-    L = seq_len(p, b);
+    L = p.batch <= 64 ? __builtin_amdgcn_readlane(s.lane_len, b) : seq_len(p, b);
     nb = blocks_of(p, L);
   }
   if (nb == 0) return false;                 // not reached: F < end <= T
