@@ -16,15 +16,11 @@ namespace {
 
 constexpr int kFusedThreads = 256;   // at most four waves per workgroup
 
-// The matrix-core body is tuned for three waves per SIMD (<= 168 registers);
-// the VALU body at groups of 2 and head_dim 128 needs a few more, so that
-// instantiation runs at two.
-template <int D, int G>
-constexpr int fused_waves_per_eu() { return (G == 2 && D == 128) ? 2 : PA_MFMA_WAVES_PER_EU; }
-
+// Three waves per SIMD (<= 168 registers), which the matrix-core body is
+// tuned for and the VALU body fits.
 template <int D, int G, int KV>
 __global__ __launch_bounds__(kFusedThreads)
-__attribute__((amdgpu_waves_per_eu(fused_waves_per_eu<D, G>())))
+__attribute__((amdgpu_waves_per_eu(PA_MFMA_WAVES_PER_EU)))
 void shared_prefix_kernel(const DecodeParams ps, const DecodeParams pp, int prefix_groups) {
   const int wg = (int)blockIdx.x;
   if (wg < prefix_groups) {
