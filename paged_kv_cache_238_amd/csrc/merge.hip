@@ -51,7 +51,9 @@ __device__ __forceinline__ float block_max(float x, float* s_max) {
 // one per partition, or the count its balanced chunks stored in the header.
 __device__ __forceinline__ int suffix_records(const MergeParams& p, int b, int L) {
   if (L == 0) return 0;
-  if (p.header[0] == 0) return p.header[kCountsAt + b];
+  // (a count is at most rec_stride when the partition kernel wrote it; the
+  // clamp keeps any other header within the row's record slots)
+  if (p.header[0] == 0) return min(max(p.header[kCountsAt + b], 0), p.rec_stride);
   return (L + p.partition_size - 1) / p.partition_size;
 }
 
