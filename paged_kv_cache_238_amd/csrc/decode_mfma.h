@@ -462,7 +462,8 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
   }
   const int ntok = min(t_begin + seg_blocks * kBlockTokens, L) - t_begin;
   const int nfull = ntok / kBlockTokens;
-  const int tail = ntok - nfull * kBlockTokens;
+  // (the shared prefix is whole blocks: its length is a multiple of 16)
+  const int tail = PREFIX ? 0 : ntok - nfull * kBlockTokens;
 
   // Ids come from LDS in order, each read NBUF blocks before its block is
   // issued, so no block waits on a table read.
@@ -758,7 +759,7 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
     nid[slot] = lds_id(j + NBUF);
   };
   Regs T;
-  load_block(__builtin_amdgcn_readfirstlane(tail_id), tail > 0, tail, T);
+  if constexpr (!PREFIX) load_block(__builtin_amdgcn_readfirstlane(tail_id), tail > 0, tail, T);
   __builtin_amdgcn_sched_barrier(0);
   // The prologue's loads stay in block order after the partial block's, so
   // each block's wait counts only the blocks issued after it.
