@@ -1,6 +1,6 @@
 """CPU fp64 oracle for paged decode attention.
 
-TEST INFRASTRUCTURE ONLY: imported by the tests, the graft smoke check and the
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check (__graft_entry__.smoke) and the
 benchmark's CPU-baseline leg; never by the HIP library or its binding.
 
 Pin status: every function here is pinned by a CPU test against something

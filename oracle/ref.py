@@ -1,7 +1,7 @@
 """CPU fp64 oracle for paged-attention decode over a block-paged KV cache.
 
 TEST INFRASTRUCTURE ONLY.  This module is imported by the tests, by the smoke
-check of the graft entry point and by the benchmark's CPU-baseline leg, and by
+check (__graft_entry__.smoke) and by the benchmark's CPU-baseline leg, and by
 nothing else: the HIP library and its Python binding never import, call or
 link it, and it shares no code, constants or helpers with them.
 
