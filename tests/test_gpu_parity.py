@@ -541,15 +541,15 @@ def test_runs_enumerated_over_many_sequences(pa, G, int8):
         np.testing.assert_allclose(lse[live], want_lse[live], rtol=0, atol=1e-4)
 
 
-@pytest.mark.parametrize("B", [600, 60])
+@pytest.mark.parametrize("B", [600, 65, 64, 60])
 @pytest.mark.parametrize("G,kv", [(1, "fp16"), (2, "fp8"), (8, "fp16"), (8, "int8")])
 def test_chunks_spanning_many_sequences(pa, G, kv, B):
     """Many one-block sequences (with empty ones between them): each balanced
     chunk of 16 blocks crosses up to 16 sequence boundaries, so one wave
     streams many short segments and writes a record for each, and a
-    sequence's blocks may sit in two chunks.  At 60 sequences a segment
-    switch takes the next length from the lanes that located the chunk
-    (batches of up to 64), at 600 from memory."""
+    sequence's blocks may sit in two chunks.  Up to 64 sequences a segment
+    switch takes the next length from the lanes that located the chunk, from
+    65 on from memory."""
     over = dict(batch=B, q_heads=G * 2, kv_heads=2, head_dim=128, lmin=1, lmax=40,
                 occupancy=0.9, kv_dtype=kv)
     wl = gen.make("gqa70b_mixed", seed=1100 + G + len(kv) + B, overrides=over)
