@@ -364,14 +364,16 @@ int pa_decode_append_fp8(void* out, float* lse_out, const void* q, const void* k
  *                                       for one kv head and merges them
  *                                       online, one record per sequence.
  *                                       The header takes 256-byte units.
- *   float2 ml[batch][q_heads][n_part+1] (m, l): m = a reference point in
+ *   float2 ml[n_part+1][batch][q_heads] (m, l), record-major (slot r of
+ *                                       every (b, h) row together): m = a
+ *                                       reference point in
  *                                       log2 units, at most the record's
  *                                       largest score s = scale * log2(e) *
  *                                       q.k (and within 8 of it); l = sum of
  *                                       2^(s - m); m + log2(l) is the
  *                                       record's log-sum-exp
  *                                       (256-byte aligned after the header)
- *   fp16   u[batch][q_heads][n_part+1][head_dim]  normalised output of the
+ *   fp16   u[n_part+1][batch][q_heads][head_dim]  normalised output of the
  *                                       record, sum 2^(s-m) v / l, rounded
  *                                       to nearest even (a convex
  *                                       combination of V rows, so within

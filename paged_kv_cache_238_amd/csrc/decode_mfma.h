@@ -709,8 +709,9 @@ __device__ __forceinline__ void mfma_body(const DecodeParams& p, const int wg) {
         if (lg == 0 && p.lse) p.lse[row] = (M + log2f(den)) * kLn2;
       } else {
         // o / l in fp16 (a convex combination of V rows, so within V's
-        // range); (m, l) stay fp32.
-        const size_t rec = row * p.rec_stride + ridx;
+        // range); (m, l) stay fp32.  Records are stored record-major (slot
+        // ridx of every row together), so a wave's G rows are one run.
+        const size_t rec = (size_t)ridx * ((size_t)p.batch * Hq) + row;
         const float inv = inv_l;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {

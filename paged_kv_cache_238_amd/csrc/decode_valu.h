@@ -428,7 +428,7 @@ __device__ __forceinline__ void valu_body(const DecodeParams& p, const int wg) {
         } else {
           // o / l in fp16 (a convex combination of V rows, so within V's
           // range); (m, l) stay fp32.
-          const size_t rec = row * p.rec_stride + ridx;
+          const size_t rec = (size_t)ridx * ((size_t)p.batch * Hq) + row;   // record-major
           const float inv = 1.0f / den;
           uint4 pk;
           uint32_t* pw = reinterpret_cast<uint32_t*>(&pk);

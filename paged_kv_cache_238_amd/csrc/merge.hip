@@ -104,13 +104,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
     if (tid == 0 && p.lse) p.lse[row] = kNegInf;
     return;
   }
-  const float2* ml = p.part_ml + row * p.rec_stride;
-  const uint2* o = reinterpret_cast<const uint2*>(p.part_o + row * p.rec_stride * D);
-  const float2* ml2 = n_pre ? p.pre_ml + row * n_pre : nullptr;
-  const uint2* o2 = n_pre ? reinterpret_cast<const uint2*>(p.pre_o + row * n_pre * D) : nullptr;
-  auto rec_ml = [&](int i) { return i < n_suf ? ml[i] : ml2[i - n_suf]; };
+  // Record-major sets: record i of this row sits i * rows entries in.
+  const size_t rows = (size_t)p.batch * p.q_heads;
+  const float2* ml = p.part_ml + row;
+  const uint2* o = reinterpret_cast<const uint2*>(p.part_o + row * D);
+  const float2* ml2 = n_pre ? p.pre_ml + row : nullptr;
+  const uint2* o2 = n_pre ? reinterpret_cast<const uint2*>(p.pre_o + row * D) : nullptr;
+  auto rec_ml = [&](int i) { return i < n_suf ? ml[i * rows] : ml2[(i - n_suf) * rows]; };
   auto rec_o = [&](int i) {
-    return i < n_suf ? o[(size_t)i * COLS + col] : o2[(size_t)(i - n_suf) * COLS + col];
+    return i < n_suf ? o[(size_t)i * rows * COLS + col] : o2[(size_t)(i - n_suf) * rows * COLS + col];
   };
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -198,10 +200,12 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(const MergeParams 
     if (lane == 0 && p.lse) p.lse[row] = kNegInf;
     return;
   }
-  const float2* ml = p.part_ml + row * p.rec_stride;
-  const uint2* o = reinterpret_cast<const uint2*>(p.part_o + row * p.rec_stride * D);
-  const float2* ml2 = n_pre ? p.pre_ml + row * n_pre : nullptr;
-  const uint2* o2 = n_pre ? reinterpret_cast<const uint2*>(p.pre_o + row * n_pre * D) : nullptr;
+  // Record-major sets: record i of this row sits i * rows entries in.
+  const size_t rows = (size_t)p.batch * p.q_heads;
+  const float2* ml = p.part_ml + row;
+  const uint2* o = reinterpret_cast<const uint2*>(p.part_o + row * D);
+  const float2* ml2 = n_pre ? p.pre_ml + row : nullptr;
+  const uint2* o2 = n_pre ? reinterpret_cast<const uint2*>(p.pre_o + row * D) : nullptr;
   float2 r[kWaveHeld];
   uint2 v[kWaveHeld];
 #pragma unroll
@@ -210,8 +214,9 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(const MergeParams 
     r[k] = make_float2(kNegInf, 0.f);
     v[k] = make_uint2(0, 0);
     if (i < n) {
-      r[k] = i < n_suf ? ml[i] : ml2[i - n_suf];
-      v[k] = i < n_suf ? o[(size_t)i * COLS + col] : o2[(size_t)(i - n_suf) * COLS + col];
+      r[k] = i < n_suf ? ml[i * rows] : ml2[(i - n_suf) * rows];
+      v[k] = i < n_suf ? o[(size_t)i * rows * COLS + col]
+                       : o2[(size_t)(i - n_suf) * rows * COLS + col];
     }
   }
   float M = kNegInf;

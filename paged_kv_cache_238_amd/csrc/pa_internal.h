@@ -35,8 +35,8 @@ struct DecodeParams {
   const int32_t* context_lens;// [B]
   uint16_t* out;              // fp16 [B, Hq, D]  (direct mode)
   float* lse;                 // fp32 [B, Hq] or null (direct mode)
-  float2* part_ml;            // [B, Hq, rec_stride] (split mode)
-  uint16_t* part_o;           // fp16 [B, Hq, rec_stride, D], normalised (split mode)
+  float2* part_ml;            // [rec_stride, B, Hq] (split mode; record-major)
+  uint16_t* part_o;           // fp16 [rec_stride, B, Hq, D], normalised (split mode)
   int max_blocks;             // table entries per row from token_offset on
   int bt_stride;              // table row stride (entries)
   int token_offset;           // tokens [0, token_offset) of every sequence are

@@ -366,7 +366,7 @@ def test_partials_plus_merge_equals_decode(pa):
     # records against the oracle's own statistics over each record's token
     # range (log2 units).  Workspace: int32 header (record mode 0 = balanced
     # chunks, record counts from word 64 on), 256-byte aligned; then (m, l)
-    # with n_part + 1 records per row
+    # record-major: n_part + 1 slots, each holding every (b, h) row
     head = ws[:4 * (64 + wl.batch)].view(torch.int32).cpu().numpy()
     assert head[0] == 0
     ranges = _chunk_records(wl.context_lens, wl.max_context_len, wl.kv_heads, P)
@@ -374,7 +374,7 @@ def test_partials_plus_merge_equals_decode(pa):
     stride = -(-wl.max_context_len // P) + 1
     off = -(-(64 + wl.batch) * 4 // 256) * 256
     ml = ws[off:off + wl.batch * wl.q_heads * stride * 8].view(torch.float32).view(
-        wl.batch, wl.q_heads, stride, 2).cpu().numpy()
+        stride, wl.batch, wl.q_heads, 2).cpu().numpy()
     # block-level statistics from the oracle, combined over each range
     blocks = ref.ref_partials(vals["q"], vals["k_pool"], vals["v_pool"], wl.block_table,
                               wl.context_lens, wl.scale, 16, vals["k_scale"], vals["v_scale"])
@@ -383,7 +383,7 @@ def test_partials_plus_merge_equals_decode(pa):
         want = [np.logaddexp.reduce(m[t0 // 16:-(-t1 // 16)] + np.log(l[t0 // 16:-(-t1 // 16)]))
                 for t0, t1 in ranges[bb]]
         n = len(want)
-        lse_gpu = (ml[bb, h, :n, 0] + np.log2(ml[bb, h, :n, 1])) * math.log(2)
+        lse_gpu = (ml[:n, bb, h, 0] + np.log2(ml[:n, bb, h, 1])) * math.log(2)
         np.testing.assert_allclose(lse_gpu, want, rtol=0, atol=1e-4)
 
 
