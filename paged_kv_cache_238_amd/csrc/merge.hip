@@ -184,7 +184,11 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(const MergeParams 
   if (rowid >= (long long)p.batch * p.q_heads) return;
   const int b = (int)(rowid / p.q_heads);
   const size_t row = (size_t)rowid;
+  // The length and the record mode and count in one round trip (the
+  // header always holds a count slot per sequence).
   const int L = p.context_lens[b] - p.token_offset;
+  const int rec_mode = p.header[0];
+  const int rec_count = min(max(p.header[kCountsAt + b], 0), p.rec_stride);
   if (L < 0 || L > p.max_context_len) {
     for (int d = lane; d < D; d += 64) p.out[row * D + d] = 0x7E00;
     if (lane == 0 && p.lse) p.lse[row] = __builtin_nanf("");
@@ -192,7 +196,8 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(const MergeParams 
   }
   // Append mode: the row's last token is its own record in the second set;
   // a sequence with no tokens has neither.
-  const int n_suf = L > 0 ? suffix_records(p, b, L - p.len_trim) : 0;
+  const int Ls = L > 0 ? L - p.len_trim : 0;
+  const int n_suf = Ls == 0 ? 0 : rec_mode == 0 ? rec_count : (Ls + p.partition_size - 1) / p.partition_size;
   const int n_pre = (p.pre_ml && (L > 0 || !p.len_trim)) ? p.n_pre : 0;
   const int n = n_suf + n_pre;
   if (n == 0) {
